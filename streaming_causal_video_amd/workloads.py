@@ -1,0 +1,149 @@
+"""Workload shapes for the streaming chunk-attention path.
+
+Shapes follow the Wan 2.1 1.3B / Wan 2.2 14B layers at 480p (832x480, latent
+grid 30x52) and 720p (1280x720, latent grid 45x80) named in the
+implementation-details table of "StreamDiffusionV2: A Streaming System for
+Dynamic and Interactive Video Generation" (paper-review blog, section 6), in
+bf16 as in the Causal-RoPE SP paper's evaluation ("Accelerating Video
+Generation Inference with Sequential-Parallel 3D Positional Encoding Using a
+Global Time Index", section 4).  Head counts, RoPE splits, chunk and window
+lengths and start frames are the workload definitions this library is
+measured on; the pages do not print them.
+
+This module holds shapes only: no RoPE, cache or attention arithmetic.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str  # "fp32" | "bf16"
+    batch: int
+    heads: int
+    head_dim: int
+    split: Tuple[int, int, int]
+    base: float
+    grid_h: int
+    grid_w: int
+    chunk_frames: int
+    sink_frames: int
+    window_frames: int
+    t0: Tuple[int, ...]
+    seed: int
+    max_query_chunks: int = 1
+    k_outlier_frac: float = 0.0
+    k_outlier_scale: float = 1.0
+    description: str = ""
+
+    @property
+    def tokens_per_frame(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def ring_frames(self) -> int:
+        return self.window_frames + self.max_query_chunks * self.chunk_frames
+
+    @property
+    def n_slots(self) -> int:
+        return self.sink_frames + self.ring_frames
+
+    @property
+    def query_frames(self) -> int:
+        return self.max_query_chunks * self.chunk_frames
+
+    @property
+    def query_rows(self) -> int:
+        return self.query_frames * self.tokens_per_frame
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+TINY_FP32 = Workload(
+    name="tiny-fp32",
+    dtype="fp32",
+    batch=1,
+    heads=2,
+    head_dim=64,
+    split=(24, 20, 20),
+    base=10000.0,
+    grid_h=4,
+    grid_w=4,
+    chunk_frames=2,
+    sink_frames=1,
+    window_frames=4,
+    t0=(37,),
+    seed=1,
+    description="tiny fp32: 2 heads, d=64, 4x4 grid, chunk 2 frames, sink 1 + window 4, t0=37",
+)
+
+WAN13B_480P = Workload(
+    name="wan1.3b-480p",
+    dtype="bf16",
+    batch=1,
+    heads=12,
+    head_dim=128,
+    split=(44, 42, 42),
+    base=10000.0,
+    grid_h=30,
+    grid_w=52,
+    chunk_frames=3,
+    sink_frames=1,
+    window_frames=12,
+    t0=(1000,),
+    seed=2,
+    description="Wan-1.3B-shaped 480p layer: 12 heads, d=128, 1560 tokens/frame, "
+    "chunk 3 frames (4680 queries), 24960 keys, t0=1000",
+)
+
+WAN13B_480P_B4 = WAN13B_480P.with_(
+    name="wan1.3b-480p-stream4",
+    batch=4,
+    t0=(0, 250, 5000, 100000),
+    seed=3,
+    description="Wan-1.3B-shaped 480p layer, 4 streams at t0 = 0, 250, 5000, 100000",
+)
+
+WAN14B_480P = WAN13B_480P.with_(
+    name="wan14b-480p",
+    heads=40,
+    seed=4,
+    k_outlier_frac=0.01,
+    k_outlier_scale=30.0,
+    description="14B-shaped 480p layer: 40 heads, 1% of raw k entries scaled x30",
+)
+
+WAN13B_720P = WAN13B_480P.with_(
+    name="wan1.3b-720p",
+    grid_h=45,
+    grid_w=80,
+    window_frames=8,
+    t0=(20000,),
+    seed=5,
+    description="720p 1.3B-shaped layer: 3600 tokens/frame, 10800 queries, 43200 keys, t0=20000",
+)
+
+WORKLOADS = {w.name: w for w in (TINY_FP32, WAN13B_480P, WAN13B_480P_B4, WAN14B_480P, WAN13B_720P)}
+ORDERED = [TINY_FP32, WAN13B_480P, WAN13B_480P_B4, WAN14B_480P, WAN13B_720P]
+
+
+def fill_schedule(w: Workload):
+    """Calls that bring each stream's cache to the state the query chunk sees.
+
+    1. cache_init with the sink frames 0 .. S_f-1 of every stream;
+    2. one append of W frames starting at max(t0[b] - W, S_f) per stream
+       (streams near the start of the video also receive frames that lie in
+       the future of their query chunk; the block-causal mask hides them);
+    3. the query chunk itself is appended by the fused rope3d_append call.
+    Returns the list of (t0 tuple, n_frames) for step 2 (empty if W == 0).
+    """
+    if w.window_frames == 0:
+        return []
+    starts = tuple(max(t - w.window_frames, w.sink_frames) for t in w.t0)
+    return [(starts, w.window_frames)]

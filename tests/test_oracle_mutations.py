@@ -1,0 +1,126 @@
+"""Plant plausible mistakes in the oracle (CPU only) and confirm the pins
+catch each one: the pins are only worth something if they fail on a wrong
+sign, a dropped term, a swapped index or a transposed operand."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import scv_oracle as O
+
+_orig_rope3d = O.rope3d
+_orig_attention = O.attention
+_orig_frame_visible = O.frame_visible
+_orig_frame_slot = O.frame_slot
+
+
+def _rope3d_variant(sign=1.0, half_split=False, order=(0, 1, 2)):
+    def rope3d(x, pos_t, pos_h, pos_w, split, base):
+        x = np.asarray(x, dtype=np.float64)
+        out = np.empty_like(x)
+        pos = (pos_t, pos_h, pos_w)
+        lo = 0
+        for a in order:
+            width = split[a]
+            th = O.rope_angles(pos[a], width, base)
+            c, s = np.cos(th)[:, None, :], sign * np.sin(th)[:, None, :]
+            if half_split:
+                xe, xo = x[:, :, lo : lo + width // 2], x[:, :, lo + width // 2 : lo + width]
+                out[:, :, lo : lo + width // 2] = xe * c - xo * s
+                out[:, :, lo + width // 2 : lo + width] = xe * s + xo * c
+            else:
+                xe, xo = x[:, :, lo : lo + width : 2], x[:, :, lo + 1 : lo + width : 2]
+                out[:, :, lo : lo + width : 2] = xe * c - xo * s
+                out[:, :, lo + 1 : lo + width : 2] = xe * s + xo * c
+            lo += width
+        return out
+
+    return rope3d
+
+
+def _attention_variant(kind):
+    def attention(q, k, v, scale):
+        if kind == "no_scale":
+            return _orig_attention(q, k, v, 1.0)
+        if kind == "transposed_v":
+            o, lse = _orig_attention(q, k, v, scale)
+            if k.shape[0] == 0:
+                return o, lse
+            s = (np.asarray(q) @ np.asarray(k).T) * scale
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            vv = np.asarray(v)
+            if vv.shape[0] == vv.shape[1]:
+                return p @ vv.T, lse
+            return p @ vv[::-1], lse
+        if kind == "lse_no_max":
+            o, lse = _orig_attention(q, k, v, scale)
+            if k.shape[0] == 0:
+                return o, lse
+            s = (np.asarray(q) @ np.asarray(k).T) * scale
+            return o, lse - s.max(axis=1)
+        if kind == "drop_last_key":
+            if k.shape[0] > 1:
+                return _orig_attention(q, k[:-1], v[:-1], scale)
+            return _orig_attention(q, k, v, scale)
+        raise ValueError(kind)
+
+    return attention
+
+
+def _frequencies_variant(kind):
+    def rope_frequencies(d_axis, base):
+        j = np.arange(d_axis // 2, dtype=np.float64)
+        if kind == "exp_j_over_d":
+            return np.power(float(base), -j / d_axis)
+        if kind == "exp_plus_one":
+            return np.power(float(base), -(2.0 * j + 1.0) / d_axis)
+        raise ValueError(kind)
+
+    return rope_frequencies
+
+
+MUTATIONS = {
+    "rope_sin_sign": ("rope3d", _rope3d_variant(sign=-1.0)),
+    "rope_half_split_pairs": ("rope3d", _rope3d_variant(half_split=True)),
+    "rope_axis_order_hwt": ("rope3d", _rope3d_variant(order=(1, 2, 0))),
+    "freq_exponent_j_over_d": ("rope_frequencies", _frequencies_variant("exp_j_over_d")),
+    "freq_exponent_off_by_one": ("rope_frequencies", _frequencies_variant("exp_plus_one")),
+    "angles_in_fp32": (
+        "rope_angles",
+        lambda pos, d, base: (np.asarray(pos, np.float32)[..., None] * O.rope_frequencies(d, base).astype(np.float32)).astype(np.float64),
+    ),
+    "slot_without_sink_offset": ("frame_slot", lambda g, sf, R: g if g < sf else g % R),
+    "slot_sink_not_pinned": ("frame_slot", lambda g, sf, R: sf + (g % R)),
+    "window_off_by_one": ("frame_visible", lambda g, s, C, sf, W: g >= 0 and g < s + C and (g < sf or g > s - W)),
+    "not_block_causal": ("frame_visible", lambda g, s, C, sf, W: g >= 0 and (g < sf or g >= s - W)),
+    "causal_drops_own_chunk": ("frame_visible", lambda g, s, C, sf, W: g >= 0 and g < s and (g < sf or g >= s - W)),
+    "no_sink": ("frame_visible", lambda g, s, C, sf, W: g >= 0 and g < s + C and g >= s - W),
+    "attention_no_scale": ("attention", _attention_variant("no_scale")),
+    "attention_transposed_v": ("attention", _attention_variant("transposed_v")),
+    "attention_lse_dropped_max": ("attention", _attention_variant("lse_no_max")),
+    "attention_drops_a_key": ("attention", _attention_variant("drop_last_key")),
+    "merge_unweighted": (
+        "merge_partials",
+        lambda o, l: (np.asarray(o).mean(axis=0), np.logaddexp.reduce(np.asarray(l), axis=0)),
+    ),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError, KeyError, ZeroDivisionError):
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for check in pins.ALL_CHECKS:
+        check()
