@@ -1,0 +1,196 @@
+/*
+ * scv.h -- streaming chunk attention for MI355X (gfx950): 3D RoPE at a
+ * global time index, a sink-pinned ring KV cache, and block-causal
+ * attention of a new chunk of latent-frame tokens over sink + window +
+ * chunk.  Every call enqueues hand-written HIP kernels on the caller's
+ * stream; the library never allocates device memory.
+ *
+ * Sources (cited by page title and section):
+ *  - "StreamDiffusionV2: A Streaming System for Dynamic and Interactive
+ *    Video Generation" (paper-review blog), section 2 "core idea": the KV of
+ *    the initial frame(s) is a pinned global anchor (sink), the rest of the
+ *    cache is a fixed-size sliding window, and the RoPE offset is refreshed.
+ *  - "Accelerating Video Generation Inference with Sequential-Parallel 3D
+ *    Positional Encoding Using a Global Time Index" (gist.science summary),
+ *    section 2(b): the start frame of each generated block is the global
+ *    time index, so token time positions need no communication; section
+ *    2(c): RoPE cos/sin are precomputed into contiguous tables instead of a
+ *    host-side cache.
+ *
+ * Conventions (readings where the pages are silent):
+ *  - Token order inside a call is frame-major then row-major:
+ *    token n = f*P + y*grid_w + x, P = grid_h*grid_w, with global time
+ *    t = t0[b] + f, row y and column x (all 0-based).
+ *  - Head dims [0,d_t) rotate with t, [d_t,d_t+d_h) with y, the rest with x;
+ *    adjacent pairs (2j, 2j+1) of an axis block of width d_a rotate by
+ *    theta = pos * omega_j, omega_j = rope_base^(-2j/d_a): the fp64 product
+ *    of the integer position and omega_j (omega_j = libm pow of the fp64
+ *    exponent -(2j)/d_a, computed once per cache on the host); cos/sin are
+ *    evaluated in fp64 and rounded to fp32; the rotation runs in fp32 and
+ *    rounds once to the storage dtype (round to nearest even).
+ *  - Frame g < sink_frames lives in sink slot g (pinned); any later frame g
+ *    lives in ring slot sink_frames + (g mod R), R = window_frames +
+ *    max_query_chunks * chunk_frames.  Each slot is stamped with the global
+ *    frame it holds (-1 = empty).
+ *  - Query frames of stream b are t0[b] .. t0[b]+n_frames-1, grouped into
+ *    chunks of chunk_frames frames from t0[b].  A query of the chunk that
+ *    starts at frame s sees a cached frame g iff g < s + chunk_frames and
+ *    (g < sink_frames or g >= s - window_frames): block-causal at chunk
+ *    granularity over sink + window + its own chunk.  Scores are scaled by
+ *    1/sqrt(head_dim).  A query that sees no key gets O = 0, lse = -inf.
+ *
+ * Tensor layouts (device memory, caller-owned, 16-byte aligned, dense):
+ *  q, k, v, o : [batch][n_frames*P][heads][head_dim] in the cache dtype.
+ *  lse        : [batch][heads][n_frames*P] fp32 (natural log).
+ *  t0         : HOST array int64[batch], read during the call only and passed
+ *               to the kernels by value (no host sync, no device read).
+ *  stream     : a hipStream_t (NULL = the default stream).  All work of a call
+ *               is enqueued on it in call order; a cache must be used by one
+ *               stream at a time.
+ *
+ * Errors: every entry point validates its arguments first and returns a
+ * negative scv_status with nothing enqueued; SCV_E_HIP reports a failed
+ * launch (message in scv_last_error()).  Asynchronous device faults surface
+ * at the caller's next synchronisation.  No C++ exception crosses the ABI.
+ */
+#ifndef SCV_H
+#define SCV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum scv_status {
+  SCV_OK = 0,
+  SCV_E_INVALID = -1,   /* null handle/pointer or invalid config value      */
+  SCV_E_SHAPE = -2,     /* n_frames or size out of the supported range      */
+  SCV_E_DTYPE = -3,     /* dtype / head_dim combination not supported       */
+  SCV_E_ALIGN = -4,     /* a device pointer is not 16-byte aligned          */
+  SCV_E_RANGE = -5,     /* a time index outside [0, 2^40)                   */
+  SCV_E_STATE = -6,     /* cache buffer too small for the config            */
+  SCV_E_WORKSPACE = -7, /* workspace missing or smaller than required       */
+  SCV_E_HIP = -8        /* a HIP runtime call or kernel launch failed       */
+} scv_status;
+
+typedef enum scv_dtype { SCV_FP32 = 0, SCV_BF16 = 1 } scv_dtype;
+
+/* Shape of one streaming cache; every stream of the batch shares it. */
+typedef struct scv_config {
+  int32_t batch;            /* streams B, 1..64                              */
+  int32_t heads;            /* H >= 1                                        */
+  int32_t head_dim;         /* d: 64 or 128                                  */
+  int32_t rope_split[3];    /* d_t, d_h, d_w: even, >= 2, sum = head_dim     */
+  double rope_base;         /* > 1                                           */
+  int32_t grid_h, grid_w;   /* latent grid, P = grid_h*grid_w <= 2^20        */
+  int32_t sink_frames;      /* S_f >= 0                                      */
+  int32_t window_frames;    /* W >= 0                                        */
+  int32_t chunk_frames;     /* C >= 1                                        */
+  int32_t max_query_chunks; /* k, 1..8; ring R = W + k*C; S_f + R <= 64      */
+  int32_t dtype;            /* scv_dtype                                     */
+} scv_config;
+
+/* Byte layout of the caller's cache buffer (offsets from its base). */
+typedef struct scv_cache_layout {
+  size_t total_bytes;
+  size_t stamps_offset;  /* int64 [B][n_slots]: frame held by each slot      */
+  size_t table_h_offset; /* fp32 [grid_h][d_h/2][2]: cos, sin of row angles  */
+  size_t table_w_offset; /* fp32 [grid_w][d_w/2][2]: cos, sin of col angles  */
+  size_t k_offset;       /* dtype [B][H][rows_pad][d]: rotated keys          */
+  size_t v_offset;       /* dtype [B][H][d][rows_pad]: values, transposed    */
+  int64_t n_slots;       /* S_f + R frame slots                              */
+  int64_t ring_frames;   /* R                                                */
+  int64_t slot_rows;     /* rows per slot: P rounded up to a multiple of 8   */
+  int64_t rows;          /* n_slots * slot_rows; slot s owns rows            */
+                         /* [s*slot_rows, s*slot_rows + P)                   */
+  int64_t rows_pad;      /* rows rounded up to a multiple of 64              */
+  int64_t elem_bytes;    /* 4 (fp32) or 2 (bf16)                             */
+} scv_cache_layout;
+
+typedef struct scv_cache scv_cache; /* opaque host-side descriptor */
+
+/* Bytes of device memory a cache with this config needs (0 if the config
+ * is invalid; scv_last_error() then says why). */
+size_t scv_cache_bytes(const scv_config* cfg);
+
+/* Layout of the cache buffer for this config (host only). */
+scv_status scv_cache_layout_of(const scv_config* cfg, scv_cache_layout* out);
+
+/* Create a host descriptor over a caller-owned device buffer of at least
+ * scv_cache_bytes(cfg) bytes (256-byte aligned).  No device work; the
+ * buffer must outlive the handle.  Per-cache constants are fixed here: the
+ * RoPE frequency ladders omega (fp64, libm pow).  Call scv_cache_init
+ * before any other call on the handle. */
+scv_status scv_cache_create(const scv_config* cfg, void* dev_buf, size_t bytes, scv_cache** out);
+
+/* Free the host descriptor (never the device buffer).  NULL is a no-op. */
+scv_status scv_cache_destroy(scv_cache* c);
+
+/* cache_init(sink).  Zeroes the key/value region, marks every slot empty,
+ * and computes the static fp32 cos/sin tables of the row and column axes.
+ * If sink_k and sink_v are non-NULL they hold the raw (unrotated) k and v
+ * of the sink frames 0..S_f-1 ([B][S_f*P][H][d]); they are rotated at global
+ * times 0..S_f-1 and written into the pinned sink slots (the initial frames'
+ * KV as the global anchor, StreamDiffusionV2 review, section 2). */
+scv_status scv_cache_init(scv_cache* c, const void* sink_k, const void* sink_v, void* stream);
+
+/* rope3d_apply(q, k, t0, grid).  Rotates q and/or k in place by split t/h/w
+ * RoPE at global time t0[b] + f (Causal-RoPE SP paper, section 2(b)); the
+ * spatial grid is the cache's.  Either pointer may be NULL (not both).
+ * 1 <= n_frames <= 65535, n_frames*P < 2^31. */
+scv_status scv_rope3d_apply(const scv_cache* c, void* q, void* k, const int64_t* t0, int32_t n_frames,
+                            void* stream);
+
+/* kv_append_roll(chunk).  Writes the already-rotated keys k_rot and the
+ * values v of frames t0[b] .. t0[b]+n_frames-1 into their slots (sink frames
+ * into the pinned sink, later frames into the ring, evicting what the slot
+ * held) and stamps the slots.  Among the frames of one call at most R may
+ * be ring frames.  Appending the same frames again is idempotent. */
+scv_status scv_kv_append_roll(scv_cache* c, const void* k_rot, const void* v, const int64_t* t0, int32_t n_frames,
+                              void* stream);
+
+/* Fused rope3d_apply + kv_append_roll in one kernel: q is rotated into q_rot
+ * (q_rot == q rotates in place), k is rotated and written with v into the
+ * cache; k itself is not modified.  q and q_rot may both be NULL (append
+ * only). */
+scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
+                             const int64_t* t0, int32_t n_frames, void* stream);
+
+/* Number of key splits chunk_attention will use for this request
+ * (kv_splits = 0 picks one from the device's compute-unit count; a request
+ * is capped at 64 and at the number of 64-key tiles). */
+int32_t scv_attention_splits(const scv_cache* c, int32_t n_frames, int32_t kv_splits);
+
+/* Workspace bytes chunk_attention needs for this request (0 when it runs
+ * without splits). */
+size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits);
+
+/* chunk_attention(q, cache) -> o.  Block-causal attention of the rotated
+ * queries of frames t0[b] .. t0[b]+n_frames-1 (1 <= n_frames <= k*C) over
+ * the cached frames each query may see; o gets the normalised output in
+ * the cache dtype, lse (nullable) the natural-log softmax normaliser.
+ * QK^T and PV run on MFMA (bf16 inputs with fp32 accumulation, or fp32),
+ * softmax in fp32; P is rounded to the input dtype before PV.  With more
+ * than one split each split writes normalised fp32 partials into ws and a
+ * merge kernel combines them (lse-weighted). */
+scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
+                               float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream);
+
+/* The fp32 cos/sin tables the kernels use for this request, written to the
+ * device buffer out (fp32, n_floats >= scv_rope_table_floats(c, n_frames)):
+ * [B][n_frames][d_t/2][2] for time, then [grid_h][d_h/2][2] for rows, then
+ * [grid_w][d_w/2][2] for columns.  For checking only. */
+size_t scv_rope_table_floats(const scv_cache* c, int32_t n_frames);
+scv_status scv_rope_tables(const scv_cache* c, const int64_t* t0, int32_t n_frames, float* out, size_t n_floats,
+                           void* stream);
+
+/* Message describing the last non-OK status on this thread. */
+const char* scv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCV_H */

@@ -1,0 +1,300 @@
+// 3D RoPE at a global time index, fused with the append/roll of keys and
+// values into the sink-pinned ring cache (gfx950).
+//
+// What is computed follows "Accelerating Video Generation Inference with
+// Sequential-Parallel 3D Positional Encoding Using a Global Time Index"
+// (section 2(b): the block's start frame is the global time index, so each
+// token's time position is t0 + frame offset, computed locally; section 2(c):
+// cos/sin precomputed into contiguous tables, no host-side work per step) and
+// the sink + rolling-window cache of "StreamDiffusionV2: A Streaming System
+// for Dynamic and Interactive Video Generation" (paper-review blog, section 2).
+//
+// These kernels are HBM-bound: per (token, head) row they read q, k, v once
+// and write q_rot, k_rot, v once (6 passes of d*elem bytes).  Layout choices:
+//  * one workgroup = 64 consecutive tokens of one frame x one head, so the
+//    frame (hence the ring slot and the time angle) is uniform per workgroup;
+//  * 16-byte vector loads/stores along head_dim, 16 B per lane;
+//  * values are stored transposed ([head][d][row]) so the attention kernel
+//    can feed V^T straight into the MFMA A operand; the transpose goes
+//    through LDS and leaves as 16-byte row-contiguous stores;
+//  * the time-axis cos/sin of the workgroup's frame is evaluated in fp64 at
+//    workgroup start (one entry per lane), the row/column tables are static
+//    per cache and read through L1/L2.
+#include "scv_internal.h"
+
+namespace scv {
+namespace {
+
+// cos/sin of the fp64 angle pos * omega, rounded to fp32 (round to nearest).
+__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, double omega) {
+  const double th = static_cast<double>(pos) * omega;
+  double s, c;
+  sincos(th, &s, &c);
+  return make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+
+struct TableArgs {
+  Geometry g;
+  Omegas om;
+  int64_t t0[kMaxBatch];
+  int32_t n_frames;
+  float2* out_t;  // [B][n_frames][dt/2] (nullable)
+  float2* out_h;  // [grid_h][dh/2]       (nullable)
+  float2* out_w;  // [grid_w][dw/2]       (nullable)
+};
+
+__global__ __launch_bounds__(256) void rope_tables_kernel(TableArgs a) {
+  const Geometry& g = a.g;
+  const int pt = g.dt / 2, ph = g.dh / 2, pw = g.dw / 2;
+  const int64_t n_t = a.out_t ? int64_t(g.B) * a.n_frames * pt : 0;
+  const int64_t n_h = a.out_h ? int64_t(g.grid_h) * ph : 0;
+  const int64_t n_w = a.out_w ? int64_t(g.grid_w) * pw : 0;
+  const int64_t total = n_t + n_h + n_w;
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
+    if (i < n_t) {
+      const int j = int(i % pt);
+      const int64_t bf = i / pt;
+      const int f = int(bf % a.n_frames);
+      const int b = int(bf / a.n_frames);
+      a.out_t[i] = rope_cos_sin(a.t0[b] + f, a.om.t[j]);
+    } else if (i < n_t + n_h) {
+      const int64_t r = i - n_t;
+      a.out_h[r] = rope_cos_sin(r / ph, a.om.h[r % ph]);
+    } else {
+      const int64_t r = i - n_t - n_h;
+      a.out_w[r] = rope_cos_sin(r / pw, a.om.w[r % pw]);
+    }
+  }
+}
+
+// Zero the key/value region (16-byte stores) and mark every slot empty.
+__global__ __launch_bounds__(256) void cache_reset_kernel(uint4* kv, int64_t n16, int64_t* stamps, int64_t n_stamps) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n16; i += stride) kv[i] = make_uint4(0, 0, 0, 0);
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n_stamps; i += stride) stamps[i] = -1;
+}
+
+template <typename T>
+struct Vec16;  // 16 bytes of T
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+};
+template <>
+struct Vec16<__bf16> {
+  static constexpr int N = 8;
+};
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 u, float* x) {
+  if constexpr (sizeof(T) == 4) {
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z);
+    x[3] = __uint_as_float(u.w);
+  } else {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // round to nearest even through the native conversion
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float* x) {
+  if constexpr (sizeof(T) == 4) {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+  } else {
+    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                      pack_bf16x2(x[6], x[7]));
+  }
+}
+
+constexpr int kTokTile = 64;
+
+// One workgroup: tokens [p0, p0+64) of frame f of stream b, one head.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
+  constexpr int EPV = Vec16<T>::N;      // elements per 16-byte vector
+  constexpr int TPR = D / EPV;          // threads per token row
+  constexpr int TPP = 256 / TPR;        // tokens per pass
+  constexpr int ROW_U32 = D * int(sizeof(T)) / 4 + 1;  // odd pitch: spreads banks
+  const Geometry& g = a.g;
+  const int tiles_per_frame = (g.P + kTokTile - 1) / kTokTile;
+  const int tile = blockIdx.x % tiles_per_frame;
+  const int head = blockIdx.x / tiles_per_frame;
+  const int f = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t gframe = a.t0[b] + f;
+  const int p0 = tile * kTokTile;
+  const int nvalid = min(kTokTile, g.P - p0);
+  const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
+  const bool to_cache = a.cache_k != nullptr;
+  const bool do_q = a.q_out != nullptr;
+  const bool do_k = a.k_in != nullptr;
+  const bool do_v = a.v_in != nullptr;
+  const bool need_angles = do_q || (do_k && a.rotate_k);
+
+  __shared__ float2 tab_t[kMaxAxisPairs];
+  __shared__ uint32_t vtile[kTokTile * ROW_U32];
+
+  if (need_angles && int(threadIdx.x) < pt) tab_t[threadIdx.x] = rope_cos_sin(gframe, a.omega_t[threadIdx.x]);
+
+  int64_t slot = 0;
+  if (to_cache) slot = gframe < g.S_f ? gframe : g.S_f + gframe % g.R;
+
+  __syncthreads();
+
+  const int dg = threadIdx.x % TPR;
+  const int64_t Ntok = int64_t(a.n_frames) * g.P;
+#pragma unroll 1
+  for (int pass = 0; pass < kTokTile / TPP; ++pass) {
+    const int tt = pass * TPP + int(threadIdx.x) / TPR;
+    const int p = p0 + tt;
+    const bool valid = tt < nvalid;
+    const int64_t in_off = ((int64_t(b) * Ntok + int64_t(f) * g.P + p) * g.H + head) * D + dg * EPV;
+
+    float cs[EPV / 2], sn[EPV / 2];
+    if (need_angles && valid) {
+      const int yy = p / g.grid_w, xx = p - (p / g.grid_w) * g.grid_w;
+#pragma unroll
+      for (int i = 0; i < EPV / 2; ++i) {
+        const int pj = dg * (EPV / 2) + i;
+        float2 t;
+        if (pj < pt)
+          t = tab_t[pj];
+        else if (pj < pth)
+          t = a.tab_h[yy * (g.dh / 2) + (pj - pt)];
+        else
+          t = a.tab_w[xx * (g.dw / 2) + (pj - pth)];
+        cs[i] = t.x;
+        sn[i] = t.y;
+      }
+    }
+    if (do_q && valid) {
+      float x[EPV], y[EPV];
+      unpack16<T>(*reinterpret_cast<const uint4*>(static_cast<const T*>(a.q_in) + in_off), x);
+#pragma unroll
+      for (int i = 0; i < EPV / 2; ++i) {
+        y[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
+        y[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
+      }
+      *reinterpret_cast<uint4*>(static_cast<T*>(a.q_out) + in_off) = pack16<T>(y);
+    }
+    if (do_k && valid) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + in_off);
+      uint4 outv = raw;
+      if (a.rotate_k) {
+        float x[EPV], y[EPV];
+        unpack16<T>(raw, x);
+#pragma unroll
+        for (int i = 0; i < EPV / 2; ++i) {
+          y[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
+          y[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
+        }
+        outv = pack16<T>(y);
+      }
+      if (to_cache) {
+        const int64_t row = slot * g.slot_rows + p;
+        T* dst = static_cast<T*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + row) * D + dg * EPV;
+        *reinterpret_cast<uint4*>(dst) = outv;
+      } else {
+        *reinterpret_cast<uint4*>(static_cast<T*>(a.k_out) + in_off) = outv;
+      }
+    }
+    if (do_v) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (valid) raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + in_off);
+      uint32_t* r = &vtile[tt * ROW_U32 + dg * 4];
+      r[0] = raw.x;
+      r[1] = raw.y;
+      r[2] = raw.z;
+      r[3] = raw.w;
+    }
+  }
+
+  if (do_v) {
+    __syncthreads();
+    // Transposed write: for each d, tokens p0 .. p0+nvalid (rounded up to a
+    // whole vector; rows past P up to slot_rows belong to this slot's padding).
+    constexpr int CPR = kTokTile / EPV;  // vectors per d-row
+    const int nvec = (nvalid + EPV - 1) / EPV;
+    T* vbase = static_cast<T*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad + slot * g.slot_rows + p0;
+    for (int idx = threadIdx.x; idx < D * CPR; idx += 256) {
+      const int d = idx / CPR, c = idx % CPR;
+      if (c >= nvec) continue;
+      uint4 out;
+      if constexpr (sizeof(T) == 4) {
+        out.x = vtile[(c * 4 + 0) * ROW_U32 + d];
+        out.y = vtile[(c * 4 + 1) * ROW_U32 + d];
+        out.z = vtile[(c * 4 + 2) * ROW_U32 + d];
+        out.w = vtile[(c * 4 + 3) * ROW_U32 + d];
+      } else {
+        uint32_t h[8];
+        const int sh = (d & 1) * 16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (vtile[(c * 8 + e) * ROW_U32 + (d >> 1)] >> sh) & 0xffffu;
+        out = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      }
+      *reinterpret_cast<uint4*>(vbase + int64_t(d) * g.rows_pad + c * EPV) = out;
+    }
+  }
+
+  if (to_cache && tile == 0 && head == 0 && threadIdx.x == 0) a.stamps[int64_t(b) * g.n_slots + slot] = gframe;
+}
+
+template <typename T, int D>
+hipError_t launch_rope_append_t(const RopeArgs& a, hipStream_t s) {
+  const int tiles_per_frame = (a.g.P + kTokTile - 1) / kTokTile;
+  dim3 grid(tiles_per_frame * a.g.H, a.n_frames, a.g.B);
+  hipLaunchKernelGGL((rope_append_kernel<T, D>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s) {
+  if (a.g.dtype == SCV_BF16) {
+    if (a.g.D == 128) return launch_rope_append_t<__bf16, 128>(a, s);
+    return launch_rope_append_t<__bf16, 64>(a, s);
+  }
+  if (a.g.D == 128) return launch_rope_append_t<float, 128>(a, s);
+  return launch_rope_append_t<float, 64>(a, s);
+}
+
+hipError_t launch_rope_tables(const Geometry& g, const Omegas& om, const int64_t* t0, int32_t n_frames, float* out_t,
+                              float2* out_h, float2* out_w, hipStream_t s) {
+  TableArgs a{};
+  a.g = g;
+  a.om = om;
+  a.n_frames = n_frames;
+  if (t0)
+    for (int b = 0; b < g.B; ++b) a.t0[b] = t0[b];
+  a.out_t = reinterpret_cast<float2*>(out_t);
+  a.out_h = out_h;
+  a.out_w = out_w;
+  const int64_t total = (out_t ? int64_t(g.B) * n_frames * (g.dt / 2) : 0) + int64_t(g.grid_h) * (g.dh / 2) +
+                        int64_t(g.grid_w) * (g.dw / 2);
+  const int blocks = int(std::min<int64_t>((total + 255) / 256, 1024));
+  hipLaunchKernelGGL(rope_tables_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_reset(const Geometry& g, void* kv_base, size_t kv_bytes, int64_t* stamps, hipStream_t s) {
+  const int64_t n16 = int64_t(kv_bytes / 16);
+  const int blocks = int(std::min<int64_t>((n16 + 255) / 256, 4096));
+  hipLaunchKernelGGL(cache_reset_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s, static_cast<uint4*>(kv_base),
+                     n16, stamps, int64_t(g.B) * g.n_slots);
+  return hipGetLastError();
+}
+
+}  // namespace scv

@@ -1,0 +1,501 @@
+// C ABI of the streaming chunk-attention library: argument validation, the
+// cache layout, per-cache constants and kernel launches.  Every entry point
+// validates before enqueueing anything and never lets an exception escape.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "scv_internal.h"
+
+struct scv_cache {
+  scv::Geometry g;
+  scv::Omegas om;
+  scv_cache_layout lay;
+  char* base;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+scv_status fail(scv_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a config and derives geometry + layout.  Returns SCV_OK or an
+// error status with the reason in `why`.
+scv_status derive(const scv_config* c, scv::Geometry* g, scv_cache_layout* L, std::string* why) {
+  if (!c) {
+    *why = "config is NULL";
+    return SCV_E_INVALID;
+  }
+  if (c->dtype != SCV_FP32 && c->dtype != SCV_BF16) {
+    *why = "dtype must be SCV_FP32 or SCV_BF16";
+    return SCV_E_DTYPE;
+  }
+  if (c->head_dim != 64 && c->head_dim != 128) {
+    *why = "head_dim must be 64 or 128";
+    return SCV_E_DTYPE;
+  }
+  if (c->batch < 1 || c->batch > scv::kMaxBatch) {
+    *why = "batch must be in [1, 64]";
+    return SCV_E_INVALID;
+  }
+  if (c->heads < 1 || c->heads > 65535) {
+    *why = "heads must be in [1, 65535]";
+    return SCV_E_INVALID;
+  }
+  const int dt = c->rope_split[0], dh = c->rope_split[1], dw = c->rope_split[2];
+  if (dt < 2 || dh < 2 || dw < 2 || (dt | dh | dw) & 1 || dt + dh + dw != c->head_dim) {
+    *why = "rope_split must be three even values >= 2 summing to head_dim";
+    return SCV_E_INVALID;
+  }
+  if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) {
+    *why = "rope_base must be finite and > 1";
+    return SCV_E_INVALID;
+  }
+  if (c->grid_h < 1 || c->grid_w < 1 || int64_t(c->grid_h) * c->grid_w > (int64_t(1) << 20)) {
+    *why = "grid_h, grid_w must be >= 1 with grid_h*grid_w <= 2^20";
+    return SCV_E_INVALID;
+  }
+  if (c->sink_frames < 0 || c->window_frames < 0 || c->chunk_frames < 1 || c->max_query_chunks < 1 ||
+      c->max_query_chunks > scv::kMaxQueryChunks) {
+    *why = "need sink_frames >= 0, window_frames >= 0, chunk_frames >= 1, 1 <= max_query_chunks <= 8";
+    return SCV_E_INVALID;
+  }
+  const int64_t R = int64_t(c->window_frames) + int64_t(c->max_query_chunks) * c->chunk_frames;
+  const int64_t n_slots = c->sink_frames + R;
+  if (n_slots > scv::kMaxSlots) {
+    *why = "sink_frames + window_frames + max_query_chunks*chunk_frames must be <= 64";
+    return SCV_E_INVALID;
+  }
+  const int64_t P = int64_t(c->grid_h) * c->grid_w;
+  if (P * c->chunk_frames * c->max_query_chunks >= (int64_t(1) << 31)) {
+    *why = "query rows per call must stay below 2^31";
+    return SCV_E_SHAPE;
+  }
+  g->B = c->batch;
+  g->H = c->heads;
+  g->D = c->head_dim;
+  g->dt = dt;
+  g->dh = dh;
+  g->dw = dw;
+  g->grid_h = c->grid_h;
+  g->grid_w = c->grid_w;
+  g->P = int32_t(P);
+  g->S_f = c->sink_frames;
+  g->W = c->window_frames;
+  g->C = c->chunk_frames;
+  g->k_max = c->max_query_chunks;
+  g->R = int32_t(R);
+  g->n_slots = int32_t(n_slots);
+  g->slot_rows = int64_t(align_up(size_t(P), 8));
+  g->rows = n_slots * g->slot_rows;
+  g->rows_pad = int64_t(align_up(size_t(g->rows), scv::kKeyTile));
+  g->dtype = c->dtype;
+  g->elem_bytes = c->dtype == SCV_BF16 ? 2 : 4;
+  g->base = c->rope_base;
+
+  std::memset(L, 0, sizeof(*L));
+  size_t off = 0;
+  L->stamps_offset = off;
+  off = align_up(off + size_t(g->B) * n_slots * 8, 256);
+  L->table_h_offset = off;
+  off = align_up(off + size_t(g->grid_h) * (dh / 2) * 8, 256);
+  L->table_w_offset = off;
+  off = align_up(off + size_t(g->grid_w) * (dw / 2) * 8, 256);
+  const size_t kv = size_t(g->B) * g->H * size_t(g->rows_pad) * g->D * g->elem_bytes;
+  L->k_offset = off;
+  off = align_up(off + kv, 256);
+  L->v_offset = off;
+  off = align_up(off + kv, 256);
+  L->total_bytes = off;
+  L->n_slots = n_slots;
+  L->ring_frames = R;
+  L->slot_rows = g->slot_rows;
+  L->rows = g->rows;
+  L->rows_pad = g->rows_pad;
+  L->elem_bytes = g->elem_bytes;
+  return SCV_OK;
+}
+
+scv_status check_cache(const scv_cache* c) {
+  if (!c) return fail(SCV_E_INVALID, "cache handle is NULL");
+  return SCV_OK;
+}
+
+scv_status check_times(const scv_cache* c, const int64_t* t0, int32_t n_frames) {
+  if (!t0) return fail(SCV_E_INVALID, "t0 is NULL");
+  for (int b = 0; b < c->g.B; ++b) {
+    if (t0[b] < 0 || t0[b] > scv::kMaxTime - n_frames)
+      return fail(SCV_E_RANGE, "t0[" + std::to_string(b) + "] = " + std::to_string(t0[b]) +
+                                   " puts a frame outside [0, 2^40)");
+  }
+  return SCV_OK;
+}
+
+scv_status check_ptr(const void* p, const char* name, bool required) {
+  if (!p) {
+    if (required) return fail(SCV_E_INVALID, std::string(name) + " is NULL");
+    return SCV_OK;
+  }
+  if (!aligned16(p)) return fail(SCV_E_ALIGN, std::string(name) + " is not 16-byte aligned");
+  return SCV_OK;
+}
+
+scv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SCV_OK;
+  return fail(SCV_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Ring frames among t0[b] .. t0[b]+n-1 (frames >= S_f) must fit in the ring.
+scv_status check_append_frames(const scv_cache* c, const int64_t* t0, int32_t n_frames) {
+  if (n_frames < 1) return fail(SCV_E_SHAPE, "n_frames must be >= 1");
+  for (int b = 0; b < c->g.B; ++b) {
+    const int64_t lo = t0[b], hi = t0[b] + n_frames;  // [lo, hi)
+    const int64_t sink_part = std::max<int64_t>(0, std::min<int64_t>(hi, c->g.S_f) - lo);
+    if (n_frames - sink_part > c->g.R)
+      return fail(SCV_E_SHAPE, "an append may place at most R = " + std::to_string(c->g.R) + " frames in the ring");
+  }
+  if (int64_t(n_frames) * c->g.P >= (int64_t(1) << 31)) return fail(SCV_E_SHAPE, "n_frames * P must be < 2^31");
+  return SCV_OK;
+}
+
+scv::RopeArgs base_rope_args(const scv_cache* c, const int64_t* t0, int32_t n_frames) {
+  scv::RopeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.g = c->g;
+  a.n_frames = n_frames;
+  for (int b = 0; b < c->g.B; ++b) a.t0[b] = t0[b];
+  for (int j = 0; j < c->g.dt / 2; ++j) a.omega_t[j] = c->om.t[j];
+  a.tab_h = reinterpret_cast<const float2*>(c->base + c->lay.table_h_offset);
+  a.tab_w = reinterpret_cast<const float2*>(c->base + c->lay.table_w_offset);
+  return a;
+}
+
+void set_cache_targets(const scv_cache* c, scv::RopeArgs* a) {
+  a->cache_k = c->base + c->lay.k_offset;
+  a->cache_v = c->base + c->lay.v_offset;
+  a->stamps = reinterpret_cast<int64_t*>(c->base + c->lay.stamps_offset);
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int resolve_splits(const scv_cache* c, int32_t n_frames, int32_t requested) {
+  const int tiles = int(c->g.rows_pad / scv::kKeyTile);
+  if (requested > 0) return std::max(1, std::min(std::min(requested, tiles), 64));
+  const int64_t nq = int64_t(n_frames) * c->g.P;
+  const int64_t qtiles = (nq + 127) / 128;
+  const int64_t wgs = qtiles * c->g.H * c->g.B;
+  const int cus = device_cu_count();
+  if (wgs >= cus) return 1;
+  int s = int((2 * int64_t(cus) + wgs - 1) / wgs);
+  s = std::min(s, std::max(1, tiles / 8));
+  return std::max(1, std::min(s, 16));
+}
+
+size_t workspace_bytes(const scv_cache* c, int32_t n_frames, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = size_t(c->g.B) * c->g.H * size_t(n_frames) * c->g.P;
+  return align_up(size_t(splits) * rows * c->g.D * 4, 256) + align_up(size_t(splits) * rows * 4, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t scv_cache_bytes(const scv_config* cfg) {
+  try {
+    scv::Geometry g;
+    scv_cache_layout L;
+    std::string why;
+    if (derive(cfg, &g, &L, &why) != SCV_OK) {
+      g_last_error = why;
+      return 0;
+    }
+    return L.total_bytes;
+  } catch (...) {
+    g_last_error = "internal error";
+    return 0;
+  }
+}
+
+scv_status scv_cache_layout_of(const scv_config* cfg, scv_cache_layout* out) {
+  try {
+    if (!out) return fail(SCV_E_INVALID, "out is NULL");
+    scv::Geometry g;
+    std::string why;
+    const scv_status s = derive(cfg, &g, out, &why);
+    if (s != SCV_OK) return fail(s, why);
+    return SCV_OK;
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_cache_create(const scv_config* cfg, void* dev_buf, size_t bytes, scv_cache** out) {
+  try {
+    if (!out) return fail(SCV_E_INVALID, "out is NULL");
+    *out = nullptr;
+    scv::Geometry g;
+    scv_cache_layout L;
+    std::string why;
+    const scv_status s = derive(cfg, &g, &L, &why);
+    if (s != SCV_OK) return fail(s, why);
+    if (!dev_buf) return fail(SCV_E_INVALID, "dev_buf is NULL");
+    if (reinterpret_cast<uintptr_t>(dev_buf) & 255u) return fail(SCV_E_ALIGN, "dev_buf must be 256-byte aligned");
+    if (bytes < L.total_bytes)
+      return fail(SCV_E_STATE, "cache buffer holds " + std::to_string(bytes) + " bytes, config needs " +
+                                   std::to_string(L.total_bytes));
+    scv_cache* c = new (std::nothrow) scv_cache;
+    if (!c) return fail(SCV_E_INVALID, "out of host memory");
+    std::memset(c, 0, sizeof(*c));
+    c->g = g;
+    c->lay = L;
+    c->base = static_cast<char*>(dev_buf);
+    // omega_{a,j} = base^(-2j/d_a): one libm pow of the fp64 exponent each.
+    for (int j = 0; j < g.dt / 2; ++j) c->om.t[j] = std::pow(g.base, -(2.0 * j) / double(g.dt));
+    for (int j = 0; j < g.dh / 2; ++j) c->om.h[j] = std::pow(g.base, -(2.0 * j) / double(g.dh));
+    for (int j = 0; j < g.dw / 2; ++j) c->om.w[j] = std::pow(g.base, -(2.0 * j) / double(g.dw));
+    *out = c;
+    return SCV_OK;
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_cache_destroy(scv_cache* c) {
+  delete c;
+  return SCV_OK;
+}
+
+scv_status scv_cache_init(scv_cache* c, const void* sink_k, const void* sink_v, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((sink_k == nullptr) != (sink_v == nullptr)) return fail(SCV_E_INVALID, "give both sink_k and sink_v or neither");
+    if (sink_k && c->g.S_f == 0) return fail(SCV_E_SHAPE, "sink given but sink_frames == 0");
+    if ((s = check_ptr(sink_k, "sink_k", false)) != SCV_OK) return s;
+    if ((s = check_ptr(sink_v, "sink_v", false)) != SCV_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = hip_status(scv::launch_cache_reset(c->g, c->base + c->lay.k_offset, c->lay.total_bytes - c->lay.k_offset,
+                                                reinterpret_cast<int64_t*>(c->base + c->lay.stamps_offset), st),
+                        "cache reset launch")) != SCV_OK)
+      return s;
+    if ((s = hip_status(scv::launch_rope_tables(c->g, c->om, nullptr, 0, nullptr,
+                                                reinterpret_cast<float2*>(c->base + c->lay.table_h_offset),
+                                                reinterpret_cast<float2*>(c->base + c->lay.table_w_offset), st),
+                        "rope table launch")) != SCV_OK)
+      return s;
+    if (sink_k) {
+      int64_t zeros[scv::kMaxBatch] = {0};
+      scv::RopeArgs a = base_rope_args(c, zeros, c->g.S_f);
+      set_cache_targets(c, &a);
+      a.k_in = sink_k;
+      a.v_in = sink_v;
+      a.rotate_k = 1;
+      if ((s = hip_status(scv::launch_rope_append(a, st), "sink append launch")) != SCV_OK) return s;
+    }
+    return SCV_OK;
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_rope3d_apply(const scv_cache* c, void* q, void* k, const int64_t* t0, int32_t n_frames, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if (!q && !k) return fail(SCV_E_INVALID, "q and k are both NULL");
+    if ((s = check_ptr(q, "q", false)) != SCV_OK) return s;
+    if ((s = check_ptr(k, "k", false)) != SCV_OK) return s;
+    if (n_frames < 1 || n_frames > 65535 || int64_t(n_frames) * c->g.P >= (int64_t(1) << 31))
+      return fail(SCV_E_SHAPE, "n_frames must be in [1, 65535] with n_frames * P < 2^31");
+    if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
+    scv::RopeArgs a = base_rope_args(c, t0, n_frames);
+    a.q_in = q;
+    a.q_out = q;
+    a.k_in = k;
+    a.k_out = k;
+    a.rotate_k = 1;
+    return hip_status(scv::launch_rope_append(a, static_cast<hipStream_t>(stream)), "rope3d_apply launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_kv_append_roll(scv_cache* c, const void* k_rot, const void* v, const int64_t* t0, int32_t n_frames,
+                              void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((s = check_ptr(k_rot, "k_rot", true)) != SCV_OK) return s;
+    if ((s = check_ptr(v, "v", true)) != SCV_OK) return s;
+    if ((s = check_times(c, t0, n_frames < 1 ? 1 : n_frames)) != SCV_OK) return s;
+    if ((s = check_append_frames(c, t0, n_frames)) != SCV_OK) return s;
+    scv::RopeArgs a = base_rope_args(c, t0, n_frames);
+    set_cache_targets(c, &a);
+    a.k_in = k_rot;
+    a.v_in = v;
+    a.rotate_k = 0;
+    return hip_status(scv::launch_rope_append(a, static_cast<hipStream_t>(stream)), "kv_append_roll launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
+                             const int64_t* t0, int32_t n_frames, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((q == nullptr) != (q_rot == nullptr)) return fail(SCV_E_INVALID, "give both q and q_rot or neither");
+    if ((s = check_ptr(q, "q", false)) != SCV_OK) return s;
+    if ((s = check_ptr(q_rot, "q_rot", false)) != SCV_OK) return s;
+    if ((s = check_ptr(k, "k", true)) != SCV_OK) return s;
+    if ((s = check_ptr(v, "v", true)) != SCV_OK) return s;
+    if ((s = check_times(c, t0, n_frames < 1 ? 1 : n_frames)) != SCV_OK) return s;
+    if ((s = check_append_frames(c, t0, n_frames)) != SCV_OK) return s;
+    scv::RopeArgs a = base_rope_args(c, t0, n_frames);
+    set_cache_targets(c, &a);
+    a.q_in = q;
+    a.q_out = q_rot;
+    a.k_in = k;
+    a.v_in = v;
+    a.rotate_k = 1;
+    return hip_status(scv::launch_rope_append(a, static_cast<hipStream_t>(stream)), "rope3d_append launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+int32_t scv_attention_splits(const scv_cache* c, int32_t n_frames, int32_t kv_splits) {
+  try {
+    if (!c || n_frames < 1 || kv_splits < 0) return 0;
+    return resolve_splits(c, n_frames, kv_splits);
+  } catch (...) {
+    return 0;
+  }
+}
+
+size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits) {
+  try {
+    if (!c || n_frames < 1 || kv_splits < 0) return 0;
+    return workspace_bytes(c, n_frames, resolve_splits(c, n_frames, kv_splits));
+  } catch (...) {
+    return 0;
+  }
+}
+
+scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
+                               float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((s = check_ptr(q_rot, "q_rot", true)) != SCV_OK) return s;
+    if ((s = check_ptr(o, "o", true)) != SCV_OK) return s;
+    if ((s = check_ptr(lse, "lse", false)) != SCV_OK) return s;
+    if (n_frames < 1 || n_frames > c->g.k_max * c->g.C)
+      return fail(SCV_E_SHAPE, "n_frames must be in [1, max_query_chunks*chunk_frames]");
+    if (kv_splits < 0) return fail(SCV_E_INVALID, "kv_splits must be >= 0");
+    if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
+    const int splits = resolve_splits(c, n_frames, kv_splits);
+    const size_t need = workspace_bytes(c, n_frames, splits);
+    if (need > 0) {
+      if (!ws) return fail(SCV_E_WORKSPACE, "workspace is NULL; need " + std::to_string(need) + " bytes");
+      if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SCV_E_ALIGN, "workspace must be 256-byte aligned");
+      if (ws_bytes < need)
+        return fail(SCV_E_WORKSPACE, "workspace holds " + std::to_string(ws_bytes) + " bytes; need " +
+                                         std::to_string(need));
+    }
+    scv::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.g = c->g;
+    a.q = q_rot;
+    a.o = o;
+    a.lse = lse;
+    a.cache_k = c->base + c->lay.k_offset;
+    a.cache_v = c->base + c->lay.v_offset;
+    a.stamps = reinterpret_cast<const int64_t*>(c->base + c->lay.stamps_offset);
+    a.n_frames = n_frames;
+    a.Nq = n_frames * c->g.P;
+    a.n_qtiles = (a.Nq + 127) / 128;
+    a.splits = splits;
+    a.tiles_total = int32_t(c->g.rows_pad / scv::kKeyTile);
+    a.tiles_per_split = (a.tiles_total + splits - 1) / splits;
+    a.scale_ln = float(1.0 / std::sqrt(double(c->g.D)));
+    a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(c->g.D)));
+    for (int b = 0; b < c->g.B; ++b) a.t0[b] = t0[b];
+    if (splits > 1) {
+      const size_t rows = size_t(c->g.B) * c->g.H * size_t(a.Nq);
+      a.part_o = static_cast<float*>(ws);
+      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(splits) * rows * c->g.D * 4, 256));
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = hip_status(scv::launch_chunk_attention(a, st), "chunk_attention launch")) != SCV_OK) return s;
+    if (splits > 1) {
+      scv::MergeArgs m;
+      m.part_o = a.part_o;
+      m.part_lse = a.part_lse;
+      m.o = o;
+      m.lse = lse;
+      m.splits = splits;
+      m.Nq = a.Nq;
+      m.g = c->g;
+      if ((s = hip_status(scv::launch_attn_merge(m, st), "attn_merge launch")) != SCV_OK) return s;
+    }
+    return SCV_OK;
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+size_t scv_rope_table_floats(const scv_cache* c, int32_t n_frames) {
+  if (!c || n_frames < 1) return 0;
+  return 2 * (size_t(c->g.B) * n_frames * (c->g.dt / 2) + size_t(c->g.grid_h) * (c->g.dh / 2) +
+              size_t(c->g.grid_w) * (c->g.dw / 2));
+}
+
+scv_status scv_rope_tables(const scv_cache* c, const int64_t* t0, int32_t n_frames, float* out, size_t n_floats,
+                           void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((s = check_ptr(out, "out", true)) != SCV_OK) return s;
+    if (n_frames < 1 || n_frames > 65535) return fail(SCV_E_SHAPE, "n_frames must be in [1, 65535]");
+    if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
+    const size_t need = scv_rope_table_floats(c, n_frames);
+    if (n_floats < need) return fail(SCV_E_SHAPE, "out holds fewer than " + std::to_string(need) + " floats");
+    const size_t nt = size_t(c->g.B) * n_frames * (c->g.dt / 2);
+    const size_t nh = size_t(c->g.grid_h) * (c->g.dh / 2);
+    float2* base = reinterpret_cast<float2*>(out);
+    return hip_status(scv::launch_rope_tables(c->g, c->om, t0, n_frames, out, base + nt, base + nt + nh,
+                                              static_cast<hipStream_t>(stream)),
+                      "rope table launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+const char* scv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "scv.h"
+
+namespace scv {
+
+constexpr int kMaxBatch = 64;
+constexpr int kMaxSlots = 64;
+constexpr int kMaxAxisPairs = 64;  // d_a / 2 <= head_dim / 2 <= 64
+constexpr int kMaxQueryChunks = 8;
+constexpr int kKeyTile = 64;       // rows per attention key tile
+constexpr int64_t kMaxTime = int64_t(1) << 40;
+
+// Everything about a cache that kernels need, resolved once on the host.
+struct Geometry {
+  int32_t B, H, D, dt, dh, dw;
+  int32_t grid_h, grid_w, P;
+  int32_t S_f, W, C, k_max, R, n_slots;
+  int64_t slot_rows, rows, rows_pad;
+  int32_t dtype;  // scv_dtype
+  int32_t elem_bytes;
+  double base;
+};
+
+// fp64 frequency ladders omega_{a,j} = base^(-2j/d_a), passed by value.
+struct Omegas {
+  double t[kMaxAxisPairs];
+  double h[kMaxAxisPairs];
+  double w[kMaxAxisPairs];
+};
+
+// Rotation / append kernel arguments (by value).
+struct RopeArgs {
+  const void* q_in;
+  void* q_out;       // null: no query work
+  const void* k_in;
+  void* k_out;       // k destination when not appending (in-place rope)
+  const void* v_in;  // null: no values
+  void* cache_k;     // null: no append
+  void* cache_v;
+  int64_t* stamps;
+  const float2* tab_h;
+  const float2* tab_w;
+  int32_t n_frames;
+  int32_t rotate_k;  // 0: k is already rotated (kv_append_roll)
+  Geometry g;
+  int64_t t0[kMaxBatch];
+  double omega_t[kMaxAxisPairs];
+};
+
+// Attention kernel arguments (by value).
+struct AttnArgs {
+  const void* q;
+  void* o;          // final output (splits == 1)
+  float* lse;       // nullable final lse (splits == 1)
+  float* part_o;    // [splits][B][H][Nq][D] fp32 (splits > 1)
+  float* part_lse;  // [splits][B][H][Nq]
+  const void* cache_k;
+  const void* cache_v;
+  const int64_t* stamps;
+  int32_t n_frames;
+  int32_t Nq;             // n_frames * P query rows per stream
+  int32_t n_qtiles;
+  int32_t splits;
+  int32_t tiles_total;    // rows_pad / kKeyTile
+  int32_t tiles_per_split;
+  float scale_log2;       // log2(e) / sqrt(D)
+  float scale_ln;         // 1 / sqrt(D)
+  Geometry g;
+  int64_t t0[kMaxBatch];
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int32_t splits;
+  int32_t Nq;
+  Geometry g;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
+hipError_t launch_rope_tables(const Geometry& g, const Omegas& om, const int64_t* t0, int32_t n_frames,
+                              float* out_t, float2* out_h, float2* out_w, hipStream_t s);
+hipError_t launch_cache_reset(const Geometry& g, void* kv_base, size_t kv_bytes, int64_t* stamps, hipStream_t s);
+hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace scv

@@ -11,6 +11,8 @@ This module contains no RoPE, cache or attention arithmetic.
 """
 from __future__ import annotations
 
+from collections import OrderedDict
+
 import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_K_OUTLIER = 0, 1, 2, 3
@@ -25,9 +27,12 @@ def _gen(seed: int, stream: int, tensor: int, frame: int) -> np.random.Generator
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """fp64 -> fp32 -> bf16, both round-to-nearest-even; returned as fp64."""
     f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    u = f.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    u += r  # finite inputs only: no carry out of 32 bits
+    u &= np.uint32(0xFFFF0000)
+    return f.astype(np.float64)
 
 
 def round_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -38,13 +43,39 @@ def round_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+_MEMO: "OrderedDict[tuple, np.ndarray]" = OrderedDict()
+_MEMO_BUDGET = 3 << 30  # bytes of generated frames kept for reuse
+_memo_bytes = 0
+
+
 def frame_tensor(w, tensor: int, stream: int, frame: int) -> np.ndarray:
-    """One frame of q, k or v for one stream: [P, H, d] fp64 (dtype-exact)."""
+    """One frame of q, k or v for one stream: [P, H, d] fp64 (dtype-exact).
+
+    Generated frames are kept in a small LRU (read-only arrays) so that two
+    consumers of the same frame in one process draw it once."""
+    global _memo_bytes
+    key = (w.seed, w.dtype, w.tokens_per_frame, w.heads, w.head_dim, w.k_outlier_frac, w.k_outlier_scale,
+           int(tensor), int(stream), int(frame))
+    hit = _MEMO.get(key)
+    if hit is not None:
+        _MEMO.move_to_end(key)
+        return hit
+    x = _draw(w, tensor, stream, frame)
+    x.setflags(write=False)
+    _MEMO[key] = x
+    _memo_bytes += x.nbytes
+    while _memo_bytes > _MEMO_BUDGET and len(_MEMO) > 1:
+        _, old = _MEMO.popitem(last=False)
+        _memo_bytes -= old.nbytes
+    return x
+
+
+def _draw(w, tensor: int, stream: int, frame: int) -> np.ndarray:
     shape = (w.tokens_per_frame, w.heads, w.head_dim)
     x = _gen(w.seed, stream, tensor, frame).standard_normal(shape)
     if tensor == TENSOR_K and w.k_outlier_frac > 0.0:
         u = _gen(w.seed, stream, TENSOR_K_OUTLIER, frame).random(shape)
-        x = np.where(u < w.k_outlier_frac, x * w.k_outlier_scale, x)
+        x[u < w.k_outlier_frac] *= w.k_outlier_scale
     return round_dtype(x, w.dtype)
 
 

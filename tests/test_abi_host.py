@@ -1,0 +1,203 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function include/scv.h declares, size
+and lay out caches as documented, and reject bad arguments with the right
+status before anything reaches the GPU.  Device pointers below are fake
+host integers: every call here must fail validation (or be host-only)
+before touching them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from streaming_causal_video_amd import binding as B
+from streaming_causal_video_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scv.h")
+
+FAKE = 1 << 40  # 256-byte aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(scv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGNATURES), "binding and header disagree"
+
+
+def test_layout_of_workloads(lib):
+    expect_rows = {
+        "tiny-fp32": (7, 16, 112, 128),
+        "wan1.3b-480p": (16, 1560, 24960, 24960),
+        "wan1.3b-480p-stream4": (16, 1560, 24960, 24960),
+        "wan14b-480p": (16, 1560, 24960, 24960),
+        "wan1.3b-720p": (12, 3600, 43200, 43200),
+    }
+    for w in W.ORDERED:
+        cfg = B.config_for(w)
+        L = B.cache_layout(cfg)
+        n_slots, slot_rows, rows, rows_pad = expect_rows[w.name]
+        assert (L.n_slots, L.slot_rows, L.rows, L.rows_pad) == (n_slots, slot_rows, rows, rows_pad), w.name
+        eb = 4 if w.dtype == "fp32" else 2
+        kv = w.batch * w.heads * rows_pad * w.head_dim * eb
+        assert L.v_offset - L.k_offset >= kv
+        assert L.total_bytes >= L.v_offset + kv
+        for off in (L.stamps_offset, L.table_h_offset, L.table_w_offset, L.k_offset, L.v_offset):
+            assert off % 256 == 0
+        assert B.cache_bytes(cfg) == L.total_bytes
+
+
+def test_odd_grid_pads_slots(lib):
+    cfg = B.make_config(batch=2, heads=3, head_dim=64, split=(24, 20, 20), base=1e4, grid_h=3, grid_w=5,
+                        sink_frames=1, window_frames=3, chunk_frames=2, dtype="bf16")
+    L = B.cache_layout(cfg)
+    assert L.slot_rows == 16 and L.n_slots == 6 and L.rows == 96 and L.rows_pad == 128
+
+
+BAD_CONFIGS = [
+    ("dtype", dict(dtype=7), B.STATUS_NAMES[-3]),
+    ("head_dim", dict(head_dim=96, split=(32, 32, 32)), "SCV_E_DTYPE"),
+    ("split_sum", dict(split=(44, 42, 40)), "SCV_E_INVALID"),
+    ("split_odd", dict(split=(43, 43, 42)), "SCV_E_INVALID"),
+    ("base", dict(base=1.0), "SCV_E_INVALID"),
+    ("batch0", dict(batch=0), "SCV_E_INVALID"),
+    ("batch65", dict(batch=65), "SCV_E_INVALID"),
+    ("grid", dict(grid_h=0), "SCV_E_INVALID"),
+    ("slots", dict(window_frames=61), "SCV_E_INVALID"),
+    ("chunks", dict(max_query_chunks=9), "SCV_E_INVALID"),
+]
+
+
+def good_kwargs():
+    return dict(batch=1, heads=12, head_dim=128, split=(44, 42, 42), base=1e4, grid_h=30, grid_w=52,
+                sink_frames=1, window_frames=12, chunk_frames=3, max_query_chunks=1, dtype="bf16")
+
+
+@pytest.mark.parametrize("name,change,status", BAD_CONFIGS, ids=[c[0] for c in BAD_CONFIGS])
+def test_bad_config_rejected(lib, name, change, status):
+    kw = good_kwargs()
+    kw.update(change)
+    cfg = B.make_config(**kw)
+    assert lib.scv_cache_bytes(ctypes.byref(cfg)) == 0
+    assert B.last_error()
+    h = ctypes.c_void_p()
+    st = lib.scv_cache_create(ctypes.byref(cfg), FAKE, 1 << 34, ctypes.byref(h))
+    assert B.STATUS_NAMES[st] == status
+    assert not h.value
+
+
+def make_handle(lib, **change):
+    kw = good_kwargs()
+    kw.update(change)
+    cfg = B.make_config(**kw)
+    n = B.cache_bytes(cfg)
+    h = ctypes.c_void_p()
+    assert lib.scv_cache_create(ctypes.byref(cfg), FAKE, n, ctypes.byref(h)) == 0, B.last_error()
+    return cfg, h
+
+
+def test_create_checks_buffer(lib):
+    cfg = B.make_config(**good_kwargs())
+    n = B.cache_bytes(cfg)
+    h = ctypes.c_void_p()
+    assert lib.scv_cache_create(ctypes.byref(cfg), FAKE + 16, n, ctypes.byref(h)) == -4
+    assert lib.scv_cache_create(ctypes.byref(cfg), FAKE, n - 1, ctypes.byref(h)) == -6
+    assert lib.scv_cache_create(ctypes.byref(cfg), None, n, ctypes.byref(h)) == -1
+    assert lib.scv_cache_destroy(None) == 0
+
+
+def t0(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_rope_apply_validation(lib):
+    cfg, h = make_handle(lib)
+    q = FAKE + (1 << 36)
+    assert lib.scv_rope3d_apply(None, q, q, t0(5), 3, None) == -1
+    assert lib.scv_rope3d_apply(h, None, None, t0(5), 3, None) == -1
+    assert lib.scv_rope3d_apply(h, q + 8, None, t0(5), 3, None) == -4
+    assert lib.scv_rope3d_apply(h, q, None, t0(-1), 3, None) == -5
+    assert lib.scv_rope3d_apply(h, q, None, t0((1 << 40) - 2), 3, None) == -5
+    assert lib.scv_rope3d_apply(h, q, None, t0(5), 0, None) == -2
+    assert lib.scv_rope3d_apply(h, q, None, t0(5), 65536, None) == -2
+    assert lib.scv_rope3d_apply(h, q, None, None, 3, None) == -1
+    lib.scv_cache_destroy(h)
+
+
+def test_append_validation(lib):
+    cfg, h = make_handle(lib)  # R = 15, S_f = 1
+    k = FAKE + (1 << 36)
+    assert lib.scv_kv_append_roll(h, None, k, t0(5), 3, None) == -1
+    assert lib.scv_kv_append_roll(h, k, k + 4, t0(5), 3, None) == -4
+    assert lib.scv_kv_append_roll(h, k, k, t0(5), 16, None) == -2  # 16 ring frames > R
+    assert lib.scv_kv_append_roll(h, k, k, t0(5), 0, None) == -2
+    assert lib.scv_rope3d_append(h, k, None, k, k, t0(5), 3, None) == -1  # q without q_rot
+    assert lib.scv_rope3d_append(h, None, None, k, k, t0(-3), 3, None) == -5
+    assert lib.scv_rope3d_append(h, None, None, k, None, t0(0), 3, None) == -1
+    lib.scv_cache_destroy(h)
+
+
+def test_append_counts_sink_frames_apart(lib):
+    # frames 0..15 at t0 = 0: frame 0 goes to the sink, 15 to the ring (= R):
+    # passes validation; with the GPU absent the launch is not attempted here,
+    # so check only the ring-capacity rule through a frame count of 17.
+    cfg, h = make_handle(lib)
+    k = FAKE + (1 << 36)
+    assert lib.scv_kv_append_roll(h, k, k, t0(0), 17, None) == -2
+    lib.scv_cache_destroy(h)
+
+
+def test_attention_validation(lib):
+    cfg, h = make_handle(lib)
+    q = FAKE + (1 << 36)
+    assert lib.scv_chunk_attention(h, q, t0(1000), 4, q, None, 1, None, 0, None) == -2  # > k*C frames
+    assert lib.scv_chunk_attention(h, q, t0(1000), 0, q, None, 1, None, 0, None) == -2
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, None, None, 1, None, 0, None) == -1
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, q + 4, 1, None, 0, None) == -4
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -1, None, 0, None) == -1
+    need = lib.scv_attention_workspace_bytes(h, 3, 4)
+    assert need > 0
+    assert lib.scv_attention_splits(h, 3, 4) == 4
+    assert lib.scv_attention_workspace_bytes(h, 3, 1) == 0
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, 4, None, 0, None) == -7
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, 4, q, need - 1, None) == -7
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, 4, q + 16, need, None) == -4
+    assert lib.scv_chunk_attention(h, q, t0(-5), 3, q, None, 4, q, need, None) == -5
+    # the split request is capped by the tile count and by 64
+    assert lib.scv_attention_splits(h, 3, 1000) == 64
+    lib.scv_cache_destroy(h)
+
+
+def test_workspace_bytes_formula(lib):
+    cfg, h = make_handle(lib)
+    rows = 1 * 12 * 4680
+    assert lib.scv_attention_workspace_bytes(h, 3, 3) == 3 * rows * 128 * 4 + (-(-(3 * rows * 4) // 256) * 256)
+    lib.scv_cache_destroy(h)
+
+
+def test_table_floats(lib):
+    cfg, h = make_handle(lib, batch=4)
+    assert lib.scv_rope_table_floats(h, 3) == 2 * (4 * 3 * 22 + 30 * 21 + 52 * 21)
+    lib.scv_cache_destroy(h)
+
+
+def test_last_error_is_set(lib):
+    cfg, h = make_handle(lib)
+    assert lib.scv_rope3d_apply(h, None, None, t0(5), 3, None) == -1
+    assert "NULL" in B.last_error()
+    lib.scv_cache_destroy(h)
