@@ -40,7 +40,8 @@
  *    1/sqrt(head_dim).  A query that sees no key gets O = 0, lse = -inf.
  *
  * Tensor layouts (device memory, caller-owned, 16-byte aligned, dense):
- *  q, k, v, o : [batch][n_frames*P][heads][head_dim] in the cache dtype.
+ *  q, k, v, o : [batch][n_frames*P][heads][head_dim] in the cache dtype;
+ *               rotated q and k (q_rot, k_rot) in the cache's qk_dtype.
  *  lse        : [batch][heads][n_frames*P] fp32 (natural log).
  *  t0         : HOST array int64[batch], read during the call only and passed
  *               to the kernels by value (no host sync, no device read).
@@ -75,7 +76,7 @@ typedef enum scv_status {
   SCV_E_HIP = -8        /* a HIP runtime call or kernel launch failed       */
 } scv_status;
 
-typedef enum scv_dtype { SCV_FP32 = 0, SCV_BF16 = 1 } scv_dtype;
+typedef enum scv_dtype { SCV_FP32 = 0, SCV_BF16 = 1, SCV_FP16 = 2 } scv_dtype;
 
 /* Shape of one streaming cache; every stream of the batch shares it. */
 typedef struct scv_config {
@@ -89,7 +90,13 @@ typedef struct scv_config {
   int32_t window_frames;    /* W >= 0                                        */
   int32_t chunk_frames;     /* C >= 1                                        */
   int32_t max_query_chunks; /* k, 1..8; ring R = W + k*C; S_f + R <= 64      */
-  int32_t dtype;            /* scv_dtype                                     */
+  int32_t dtype;            /* scv_dtype of q, k, v, o (SCV_FP32, SCV_BF16)  */
+  int32_t qk_dtype;         /* format of the ROTATED q and k (q_rot, cached  */
+                            /* keys) and of the QK^T MFMA operands:          */
+                            /* 0 = same as dtype; SCV_FP16 (dtype SCV_BF16   */
+                            /* only) keeps 3 more mantissa bits at the same  */
+                            /* MFMA rate for inputs whose rotated values     */
+                            /* stay within +-65504                           */
 } scv_config;
 
 /* Byte layout of the caller's cache buffer (offsets from its base). */
@@ -98,7 +105,7 @@ typedef struct scv_cache_layout {
   size_t stamps_offset;  /* int64 [B][n_slots]: frame held by each slot      */
   size_t table_h_offset; /* fp32 [grid_h][d_h/2][2]: cos, sin of row angles  */
   size_t table_w_offset; /* fp32 [grid_w][d_w/2][2]: cos, sin of col angles  */
-  size_t k_offset;       /* dtype [B][H][rows_pad][d]: rotated keys          */
+  size_t k_offset;       /* qk_dtype [B][H][rows_pad][d]: rotated keys       */
   size_t v_offset;       /* dtype [B][H][d][rows_pad]: values, transposed    */
   int64_t n_slots;       /* S_f + R frame slots                              */
   int64_t ring_frames;   /* R                                                */
@@ -138,23 +145,25 @@ scv_status scv_cache_init(scv_cache* c, const void* sink_k, const void* sink_v, 
 
 /* rope3d_apply(q, k, t0, grid).  Rotates q and/or k in place by split t/h/w
  * RoPE at global time t0[b] + f (Causal-RoPE SP paper, section 2(b)); the
- * spatial grid is the cache's.  Either pointer may be NULL (not both).
- * 1 <= n_frames <= 65535, n_frames*P < 2^31. */
+ * spatial grid is the cache's.  The rotated values are written in the
+ * cache's qk_dtype (with SCV_FP16 the buffers then hold fp16 values).
+ * Either pointer may be NULL (not both).  1 <= n_frames <= 65535 and
+ * n_frames*P < 2^31. */
 scv_status scv_rope3d_apply(const scv_cache* c, void* q, void* k, const int64_t* t0, int32_t n_frames,
                             void* stream);
 
-/* kv_append_roll(chunk).  Writes the already-rotated keys k_rot and the
- * values v of frames t0[b] .. t0[b]+n_frames-1 into their slots (sink frames
- * into the pinned sink, later frames into the ring, evicting what the slot
- * held) and stamps the slots.  Among the frames of one call at most R may
+/* kv_append_roll(chunk).  Writes the already-rotated keys k_rot (qk_dtype)
+ * and the values v of frames t0[b] .. t0[b]+n_frames-1 into their slots
+ * (sink frames into the pinned sink, later frames into the ring, evicting
+ * what the slot held) and stamps the slots.  Among the frames of one call at most R may
  * be ring frames.  Appending the same frames again is idempotent. */
 scv_status scv_kv_append_roll(scv_cache* c, const void* k_rot, const void* v, const int64_t* t0, int32_t n_frames,
                               void* stream);
 
 /* Fused rope3d_apply + kv_append_roll in one kernel: q is rotated into q_rot
- * (q_rot == q rotates in place), k is rotated and written with v into the
- * cache; k itself is not modified.  q and q_rot may both be NULL (append
- * only). */
+ * (qk_dtype; q_rot == q rotates in place), k is rotated and written with v
+ * into the cache; k itself is not modified.  q and q_rot may both be NULL
+ * (append only). */
 scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
                              const int64_t* t0, int32_t n_frames, void* stream);
 
@@ -168,11 +177,12 @@ int32_t scv_attention_splits(const scv_cache* c, int32_t n_frames, int32_t kv_sp
 size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits);
 
 /* chunk_attention(q, cache) -> o.  Block-causal attention of the rotated
- * queries of frames t0[b] .. t0[b]+n_frames-1 (1 <= n_frames <= k*C) over
- * the cached frames each query may see; o gets the normalised output in
- * the cache dtype, lse (nullable) the natural-log softmax normaliser.
- * QK^T and PV run on MFMA (bf16 inputs with fp32 accumulation, or fp32),
- * softmax in fp32; P is rounded to the input dtype before PV.  With more
+ * queries q_rot (qk_dtype) of frames t0[b] .. t0[b]+n_frames-1
+ * (1 <= n_frames <= k*C) over the cached frames each query may see; o gets
+ * the normalised output in the cache dtype, lse (nullable) the natural-log
+ * softmax normaliser.  QK^T and PV run on MFMA with fp32 accumulation
+ * (qk_dtype operands for QK^T; dtype operands for PV), softmax in fp32; P is
+ * rounded to the dtype before PV.  With more
  * than one split each split writes normalised fp32 partials into ws and a
  * merge kernel combines them (lse-weighted). */
 scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,

@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libscv.so")
 
-SCV_FP32, SCV_BF16 = 0, 1
+SCV_FP32, SCV_BF16, SCV_FP16 = 0, 1, 2
+_DTYPE_CODES = {"fp32": SCV_FP32, "bf16": SCV_BF16, "fp16": SCV_FP16}
 STATUS_NAMES = {
     0: "SCV_OK",
     -1: "SCV_E_INVALID",
@@ -42,6 +43,7 @@ class ScvConfig(ctypes.Structure):
         ("chunk_frames", ctypes.c_int32),
         ("max_query_chunks", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("qk_dtype", ctypes.c_int32),
     ]
 
 
@@ -130,6 +132,7 @@ def make_config(
     chunk_frames,
     max_query_chunks=1,
     dtype="bf16",
+    qk_dtype="",
 ) -> ScvConfig:
     c = ScvConfig()
     c.batch, c.heads, c.head_dim = batch, heads, head_dim
@@ -138,7 +141,8 @@ def make_config(
     c.grid_h, c.grid_w = grid_h, grid_w
     c.sink_frames, c.window_frames, c.chunk_frames = sink_frames, window_frames, chunk_frames
     c.max_query_chunks = max_query_chunks
-    c.dtype = {"fp32": SCV_FP32, "bf16": SCV_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    c.dtype = _DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    c.qk_dtype = (_DTYPE_CODES[qk_dtype] if qk_dtype else 0) if isinstance(qk_dtype, str) else int(qk_dtype)
     return c
 
 
@@ -157,6 +161,7 @@ def config_for(w) -> ScvConfig:
         chunk_frames=w.chunk_frames,
         max_query_chunks=w.max_query_chunks,
         dtype=w.dtype,
+        qk_dtype=w.qk_dtype,
     )
 
 
@@ -199,7 +204,9 @@ class Cache:
         self.layout = cache_layout(cfg)
         self.nbytes = int(self.layout.total_bytes)
         self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
-        self.dtype = torch.bfloat16 if cfg.dtype == SCV_BF16 else torch.float32
+        tmap = {SCV_FP32: torch.float32, SCV_BF16: torch.bfloat16, SCV_FP16: torch.float16}
+        self.dtype = tmap[cfg.dtype]
+        self.qk_dtype = tmap[cfg.qk_dtype or cfg.dtype]
         self.P = cfg.grid_h * cfg.grid_w
         h = _VP()
         _check(self.lib.scv_cache_create(ctypes.byref(cfg), self.buffer.data_ptr(), self.nbytes, ctypes.byref(h)),
@@ -207,13 +214,14 @@ class Cache:
         self.handle = h
 
     # -- tensor checks (marshalling) ------------------------------------
-    def _tok(self, x, n_frames, name):
+    def _tok(self, x, n_frames, name, rotated=False):
         if x is None:
             return None
         c = self.cfg
         want = (c.batch, n_frames * self.P, c.heads, c.head_dim)
-        if tuple(x.shape) != want or x.dtype != self.dtype or not x.is_cuda or not x.is_contiguous():
-            raise ValueError(f"{name}: need contiguous {self.dtype} cuda tensor {want}, got {x.dtype} {tuple(x.shape)}")
+        dt = self.qk_dtype if rotated else self.dtype
+        if tuple(x.shape) != want or x.dtype != dt or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name}: need contiguous {dt} cuda tensor {want}, got {x.dtype} {tuple(x.shape)}")
         return x
 
     # -- the four calls ---------------------------------------------------
@@ -224,6 +232,8 @@ class Cache:
         _check(self.lib.scv_cache_init(self.handle, _ptr(sink_k), _ptr(sink_v), _stream(stream)), "scv_cache_init")
 
     def rope3d_apply(self, q, k, t0, n_frames, stream=None):
+        """Rotates q and/or k in place; returns them viewed in the rotated
+        (qk) dtype, which is what their buffers hold afterwards."""
         self._tok(q, n_frames, "q")
         self._tok(k, n_frames, "k")
         _check(
@@ -231,9 +241,10 @@ class Cache:
                                       _stream(stream)),
             "scv_rope3d_apply",
         )
+        return (None if q is None else q.view(self.qk_dtype), None if k is None else k.view(self.qk_dtype))
 
     def kv_append_roll(self, k_rot, v, t0, n_frames, stream=None):
-        self._tok(k_rot, n_frames, "k_rot")
+        self._tok(k_rot, n_frames, "k_rot", rotated=True)
         self._tok(v, n_frames, "v")
         _check(
             self.lib.scv_kv_append_roll(self.handle, _ptr(k_rot), _ptr(v), _t0_array(t0, self.cfg.batch), n_frames,
@@ -243,7 +254,7 @@ class Cache:
 
     def rope3d_append(self, q, q_rot, k, v, t0, n_frames, stream=None):
         self._tok(q, n_frames, "q")
-        self._tok(q_rot, n_frames, "q_rot")
+        self._tok(q_rot, n_frames, "q_rot", rotated=True)
         self._tok(k, n_frames, "k")
         self._tok(v, n_frames, "v")
         _check(
@@ -267,7 +278,7 @@ class Cache:
     def chunk_attention(self, q_rot, t0, n_frames, o, lse=None, kv_splits=0, ws=None, stream=None):
         import torch
 
-        self._tok(q_rot, n_frames, "q_rot")
+        self._tok(q_rot, n_frames, "q_rot", rotated=True)
         self._tok(o, n_frames, "o")
         if lse is not None:
             want = (self.cfg.batch, self.cfg.heads, n_frames * self.P)
@@ -317,8 +328,8 @@ class Cache:
                 c.grid_h, dh // 2, 2),
             "table_w": buf[L.table_w_offset : L.table_w_offset + c.grid_w * (dw // 2) * 8].view(torch.float32).view(
                 c.grid_w, dw // 2, 2),
-            "k": buf[L.k_offset : L.k_offset + kv].view(self.dtype).view(c.batch, c.heads, int(L.rows_pad),
-                                                                          c.head_dim),
+            "k": buf[L.k_offset : L.k_offset + kv].view(self.qk_dtype).view(c.batch, c.heads, int(L.rows_pad),
+                                                                             c.head_dim),
             "v_t": buf[L.v_offset : L.v_offset + kv].view(self.dtype).view(c.batch, c.heads, c.head_dim,
                                                                             int(L.rows_pad)),
         }

@@ -42,6 +42,10 @@ COMMON = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (the softmax reads S and rescales O
+    # with VALU instructions; AGPR accumulators would need copies)
+    "-mllvm",
+    "-amdgpu-mfma-vgpr-form",
     "-I",
     INCLUDE,
     "-I",

@@ -36,8 +36,27 @@ namespace scv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// 8 QK^T operand elements (bf16 or fp16) and the matching 32x32x16 MFMA.
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<__bf16> {
+  typedef bf16x8 type;
+};
+template <>
+struct Vec8<_Float16> {
+  typedef halfx8 type;
+};
+__device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma_32x32x16(halfx8 a, halfx8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 constexpr int kWaves = 4;
 constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
@@ -106,32 +125,106 @@ __device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, fp32 accumulation
+// bf16 inputs, fp32 accumulation; QKT = format of the rotated q/k operands
+// (bf16, or fp16 for 3 more mantissa bits at the same MFMA rate).
+//
+// One wave owns 64 query rows as two 32-row blocks, so every K or V^T
+// fragment read from LDS feeds two MFMAs; four waves (256 rows) share each
+// 64-key tile.  Tiles are moved global -> LDS by the 16-byte direct loads
+// of gfx950 (no VGPR staging), double-buffered, one barrier per tile.
+// In LDS, K rows are permuted inside each 16-row group (bits 2 and 3 of the
+// row index swapped) so that the S^T accumulator of lane half h holds, per
+// 16-key group, exactly keys 8h..8h+7 of that group: P^T then pairs with
+// V^T read in natural key order (one 16-byte read per lane).  Both tiles
+// carry an XOR swizzle of 16-byte chunks against LDS bank conflicts.
+// Softmax rescaling is lazy: the reference max moves only when a row's
+// max grows by more than 2^8 (so exponentials stay <= 256).
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256, 2) void chunk_attn_bf16_kernel(AttnArgs a) {
-  constexpr int CH = D / 8;                  // 16-byte chunks per key row
-  constexpr int KROW = D * 2;                // bytes per key row
-  constexpr int KBYTES = kKeyTile * KROW;
-  constexpr int VROW = kKeyTile * 2;         // bytes per V^T row (64 keys)
-  constexpr int K_LOADS = kKeyTile * CH / 256;
-  constexpr int V_PAIRS = D * 4 / 256;       // (2 x 16 B) per thread per tile
-  constexpr int KS = D / 16;                 // k-steps of QK^T
-  constexpr int DB = D / 32;                 // 32-row blocks of O^T
-  static_assert(K_LOADS >= 1 && V_PAIRS >= 1, "tile sizes");
+// Direct global -> LDS load of 16 bytes per lane: lane l writes LDS byte
+// address lds_base + 16*l (lds_base wave-uniform, via M0); the source address
+// is the lane's own.  Issued through inline assembly so that the compiler does
+// not guard later LDS reads of other buffers with waits on these loads; the
+// kernel waits for them itself (vmcnt) before the barrier that publishes a
+// tile.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_base), "v"(src) : "m0", "memory");
+}
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-  __shared__ __attribute__((aligned(16))) char smem[2][KBYTES + D * VROW];
+// max / sum of x over lanes l and l ^ 32 (one v_permlane32_swap)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Empty asm that claims to modify a value: keeps the computation of x at this
+// point in the program (the optimizer may otherwise sink it past a branch to
+// its first use, out of the block whose MFMAs it is meant to overlap).
+__device__ __forceinline__ void pin(bf16x8& x) {
+  uint4 u = __builtin_bit_cast(uint4, x);
+  asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+  x = __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// LDS row r of a K tile holds key row kperm(r) of the tile.
+__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+constexpr int kQB = 2;                        // 32-query blocks per wave
+constexpr int kRowsBf16 = 32 * kQB * kWaves;  // 256 query rows per workgroup
+static_assert(kRowsBf16 == kAttnRowsBf16, "host and kernel agree on the query tile");
+constexpr int kStages = 3;                    // LDS tiles: consumed, landing, loading
+
+template <int D>
+struct Bf16Tile {
+  static constexpr int CH = D / 8;               // 16-byte chunks per K row
+  static constexpr int KROW = D * 2;             // bytes per K row
+  static constexpr int KBYTES = kKeyTile * KROW;
+  static constexpr int VROW = kKeyTile * 2;      // bytes per V^T row (64 keys)
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int K_DMA = KBYTES / 1024 / kWaves;  // 1 KB loads per wave
+  static constexpr int V_DMA = VBYTES / 1024 / kWaves;
+  static constexpr int K_ROWS_PER_DMA = 1024 / KROW;
+  static constexpr int KS = D / 16;              // k-steps of QK^T
+  static constexpr int DB = D / 32;              // 32-row blocks of O^T
+};
+
+template <int D, typename QKT>
+__global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
+  typedef typename Vec8<QKT>::type qk8;
+  typedef Bf16Tile<D> T;
+  static_assert(T::K_DMA >= 1 && T::V_DMA >= 1, "tile sizes");
+
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * T::STAGE];
   __shared__ uint64_t vis_mask[kMaxQueryChunks];
 
   const Geometry& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
   const int qtile = blockIdx.x, head = blockIdx.y;
   const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
-  const int qrow = qtile * kBlockM + wave * 32 + l32;
-  const bool qvalid = qrow < a.Nq;
+  int qrow[kQB];
+  bool qvalid[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    qrow[qb] = qtile * kRowsBf16 + wave * 64 + qb * 32 + l32;
+    qvalid[qb] = qrow[qb] < a.Nq;
+  }
 
-  const Visibility vis = compute_visibility<kBlockM>(a, b, qtile, qrow, qvalid, vis_mask);
+  const Visibility vis = compute_visibility<kRowsBf16>(a, b, qtile, qrow[0], qvalid[0], vis_mask);
+  uint64_t mine[kQB];
+  {
+    const int rows_per_chunk = g.P * g.C;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+      mine[qb] = vis_mask[qvalid[qb] ? qrow[qb] / rows_per_chunk : (qtile * kRowsBf16) / rows_per_chunk];
+  }
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, a.tiles_total);
@@ -140,169 +233,288 @@ __global__ __launch_bounds__(256, 2) void chunk_attn_bf16_kernel(AttnArgs a) {
     return t;
   };
 
-  // Q^T operand: lane (l32, hl) holds q[qrow][16*kk + 8*hl .. +8].
-  bf16x8 qf[KS];
-  {
-    const __bf16* qp =
-        static_cast<const __bf16*>(a.q) + ((int64_t(b) * a.Nq + (qvalid ? qrow : 0)) * g.H + head) * D + 8 * hl;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+  const char* kbase = static_cast<const char*>(a.cache_k) + (int64_t(b) * g.H + head) * g.rows_pad * T::KROW;
+  const char* vbase = static_cast<const char*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad * 2;
+  auto issue_tile = [&](int t, int stg) {
+    const int64_t r0 = int64_t(t) * kKeyTile;
+    const uint32_t kdst = lds0 + uint32_t(stg * T::STAGE);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8, u);
+    for (int i = 0; i < T::K_DMA; ++i) {
+      const int n = wave * T::K_DMA + i;
+      const int r = n * T::K_ROWS_PER_DMA + lane / T::CH;  // LDS row
+      const int gc = (lane % T::CH) ^ (r & (T::CH - 1));    // source chunk
+      dma16(kbase + (r0 + kperm(r)) * T::KROW + gc * 16, kdst + uint32_t(n * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < T::V_DMA; ++i) {
+      const int n = wave * T::V_DMA + i;
+      const int r = n * 8 + (lane >> 3);  // d row
+      const int gc = (lane & 7) ^ (r & 7);
+      dma16(vbase + int64_t(r) * g.rows_pad * 2 + r0 * 2 + gc * 16, kdst + uint32_t(T::KBYTES + n * 1024));
+    }
+  };
+
+  // Q^T operands: lane (l32, hl) holds q[qrow][16*kk + 8*hl .. +8].
+  qk8 qf[kQB][T::KS];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const QKT* qp = static_cast<const QKT*>(a.q) +
+                    ((int64_t(b) * a.Nq + (qvalid[qb] ? qrow[qb] : 0)) * g.H + head) * D + 8 * hl;
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) {
+      const uint4 u = qvalid[qb] ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      qf[qb][kk] = __builtin_bit_cast(qk8, u);
     }
   }
 
-  floatx16 o[DB];
+  // loop-invariant LDS byte offsets of this lane's K and V^T fragments
+  int koff[T::KS];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int kk = 0; kk < T::KS; ++kk) koff[kk] = l32 * T::KROW + (((2 * kk + hl) ^ (l32 & (T::CH - 1))) * 16);
+  int voff[4];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) voff[g4] = T::KBYTES + l32 * T::VROW + (((2 * g4 + hl) ^ (l32 & 7)) * 16);
 
-  const char* kbase = static_cast<const char*>(a.cache_k) + (int64_t(b) * g.H + head) * g.rows_pad * KROW;
-  const char* vbase = static_cast<const char*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad * 2;
-  uint4 kreg[K_LOADS];
-  uint4 vreg[V_PAIRS][2];
+  floatx16 o[kQB][T::DB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) o[qb][db] = floatx16{};
+  float m_run[kQB], l_run[kQB], msc[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+    msc[qb] = 0.f;
+  }
+  const float c = a.scale_log2;
+  const float lazy = 8.f / c;  // raw-score growth that forces a rescale (2^8)
 
-  auto gload = [&](int t) {
-    const int64_t r0 = int64_t(t) * kKeyTile;
+  // S^T of one half tile (32 keys = LDS rows 32j .. 32j+31) for both blocks
+  auto qk_half = [&](const char* st, int j, floatx16* s) {
 #pragma unroll
-    for (int j = 0; j < K_LOADS; ++j) {
-      const int i = tid + 256 * j, row = i / CH, c = i % CH;
-      kreg[j] = *reinterpret_cast<const uint4*>(kbase + (r0 + row) * KROW + c * 16);
-    }
+    for (int qb = 0; qb < kQB; ++qb) s[qb] = floatx16{};
 #pragma unroll
-    for (int j = 0; j < V_PAIRS; ++j) {
-      const int i = tid + 256 * j, row = i >> 2, gq = i & 3;
-      const char* p = vbase + int64_t(row) * g.rows_pad * 2 + (r0 + 16 * gq) * 2;
-      vreg[j][0] = *reinterpret_cast<const uint4*>(p);
-      vreg[j][1] = *reinterpret_cast<const uint4*>(p + 16);
+    for (int kk = 0; kk < T::KS; ++kk) {
+      const qk8 kf = *reinterpret_cast<const qk8*>(st + koff[kk] + j * 32 * T::KROW);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) s[qb] = mfma_32x32x16(kf, qf[qb][kk], s[qb]);
     }
   };
-  auto lds_store = [&](int stage) {
-    char* ks = smem[stage];
-    char* vs = smem[stage] + KBYTES;
-#pragma unroll
-    for (int j = 0; j < K_LOADS; ++j) {
-      const int i = tid + 256 * j, row = i / CH, c = i % CH;
-      *reinterpret_cast<uint4*>(ks + row * KROW + ((c ^ (row & (CH - 1))) * 16)) = kreg[j];
-    }
-#pragma unroll
-    for (int j = 0; j < V_PAIRS; ++j) {
-      const int i = tid + 256 * j, row = i >> 2, gq = i & 3, sw = row & 7;
-      const uint4 A = vreg[j][0], Bv = vreg[j][1];
-      *reinterpret_cast<uint4*>(vs + row * VROW + (((2 * gq) ^ sw) * 16)) = make_uint4(A.x, A.y, Bv.x, Bv.y);
-      *reinterpret_cast<uint4*>(vs + row * VROW + (((2 * gq + 1) ^ sw) * 16)) = make_uint4(A.z, A.w, Bv.z, Bv.w);
-    }
-  };
-
-  auto compute = [&](int stage, int t) {
-    const char* ks = smem[stage];
-    const char* vs = smem[stage] + KBYTES;
-    floatx16 s0 = floatx16{}, s1 = floatx16{};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int c = 2 * kk + hl;
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(ks + l32 * KROW + ((c ^ (l32 & (CH - 1))) * 16));
-      const bf16x8 k1 =
-          *reinterpret_cast<const bf16x8*>(ks + (32 + l32) * KROW + ((c ^ ((32 + l32) & (CH - 1))) * 16));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
-    }
-    // accumulator element i of lane (l32, hl) is key 8*(i/4) + 4*hl + i%4 (+32 for s1)
-    const int64_t r0 = int64_t(t) * kKeyTile;
-    const bool full = ((tile_slot_bits(g, t) & ~vis.all) == 0) && (r0 + kKeyTile <= g.rows) && (g.slot_rows == g.P);
-    if (!full) {
-      const int r0i = int(r0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 8 * (i / 4) + 4 * hl + (i & 3);
-        s0[i] = key_visible(g, vis.mine, r0i + key) ? s0[i] : -INFINITY;
-        s1[i] = key_visible(g, vis.mine, r0i + 32 + key) ? s1[i] : -INFINITY;
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float msc = (m_new == -INFINITY) ? 0.f : m_new * a.scale_log2;
-    const float alpha = fast_exp2(m_run * a.scale_log2 - msc);
-    float rs = 0.f;
-    bf16x8 pk[4];
+  // element i of a half's accumulator in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4)
+  auto mask_half = [&](int t, int j, floatx16* s) {
+    const int r0 = t * kKeyTile + 32 * j;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p0 = fast_exp2(__builtin_fmaf(s0[i], a.scale_log2, -msc));
-      const float p1 = fast_exp2(__builtin_fmaf(s1[i], a.scale_log2, -msc));
-      rs += p0 + p1;
-      pk[i / 8][i % 8] = static_cast<__bf16>(p0);
-      pk[2 + i / 8][i % 8] = static_cast<__bf16>(p1);
+      const int key = r0 + kperm(8 * (i / 4) + 4 * hl + (i & 3));
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) s[qb][i] = key_visible(g, mine[qb], key) ? s[qb][i] : -INFINITY;
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+  };
+  auto tile_full = [&](int t) {
+    const int64_t r0 = int64_t(t) * kKeyTile;
+    return ((tile_slot_bits(g, t) & ~vis.all) == 0) && (r0 + kKeyTile <= g.rows) && (g.slot_rows == g.P);
+  };
+  // P^T (bf16) of a half for both blocks; accumulates the row sums
+  auto exp_half = [&](const floatx16* s, bf16x8 (*p)[2]) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    // O^T += V^T P^T over 4 groups of 16 keys
+    for (int qb = 0; qb < kQB; ++qb) {
+      float rs = 0.f;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int row = db * 32 + l32;
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + row * VROW + ((((2 * g4) + hl) ^ (row & 7)) * 16));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[g4], o[db], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(__builtin_fmaf(s[qb][i], c, -msc[qb]));
+        rs += e;
+        p[qb][i / 8][i % 8] = static_cast<__bf16>(e);
       }
+      l_run[qb] += rs;
+    }
+  };
+  // O^T += V^T P^T for the two 16-key groups of half j
+  auto pv_half = [&](const char* st, int j, bf16x8 (*p)[2]) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[qb][gg], o[qb][db], 0, 0, 0);
+      }
+  };
+  // row max of a half; returns the candidate new maxima
+  auto max_half = [&](const floatx16* s, float* m_new) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[qb][i], s[qb][i + 1]));
+      m_new[qb] = fmaxf(m_run[qb], max_halves(mx));
+    }
+  };
+  // lazy rescale (after the PV that used the old reference max)
+  auto rescale = [&](const float* m_new) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      if (__any(m_new[qb] > m_run[qb] + lazy)) {
+        const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2((m_run[qb] - m_new[qb]) * c);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) o[qb][db] *= alpha;
+        m_run[qb] = m_new[qb];
+      }
+      msc[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
     }
   };
 
-  int t = next_tile(t_begin);
-  if (t < t_end) {
-    gload(t);
-    lds_store(0);
-  }
-  __syncthreads();
-  int stage = 0;
-  while (t < t_end) {
-    const int tn = next_tile(t + 1);
-    if (tn < t_end) gload(tn);
-    compute(stage, t);
-    if (tn < t_end) lds_store(stage ^ 1);
+  // Phase A: S^T of the next half (tile stn, half nj) on the MFMA pipe,
+  // interleaved step by step with the exponentials of the current half
+  // (sa -> P^T in p, row sums into l_run).  Source order is kept by
+  // sched_barrier so each step's VALU work sits in the shadow of its MFMAs.
+  auto phase_a = [&](const char* stn, int nj, const floatx16* sa, floatx16* sb, bf16x8 (*p)[2]) {
+    constexpr int EPS = 2 * 16 / T::KS;  // exponentials per step
+    qk8 kf[T::KS];
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) kf[kk] = *reinterpret_cast<const qk8*>(stn + koff[kk] + nj * 32 * T::KROW);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) sb[qb] = floatx16{};
+    float rs[kQB] = {0.f, 0.f};
+#pragma unroll
+    for (int step = 0; step < T::KS; ++step) {
+#pragma unroll
+      for (int e = step * EPS; e < (step + 1) * EPS; ++e) {
+        const int qb = e / 16, i = e % 16;
+        const float x = fast_exp2(__builtin_fmaf(sa[qb][i], c, -msc[qb]));
+        rs[qb] += x;
+        p[qb][i / 8][i % 8] = static_cast<__bf16>(x);
+      }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) sb[qb] = mfma_32x32x16(kf[step], qf[qb][step], sb[qb]);
+      if ((step + 1) * EPS % 8 == 0) pin(p[((step + 1) * EPS - 1) / 16][(((step + 1) * EPS - 1) % 16) / 8]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      pin(rs[qb]);
+      l_run[qb] += rs[qb];
+    }
+  };
+  // Phase B: O^T += V^T P^T of the current half (tile st, half j) on the MFMA
+  // pipe, interleaved with the row max of the next half (sb -> m_new).
+  auto phase_b = [&](const char* st, int j, bf16x8 (*p)[2], const floatx16* sb, float* m_new) {
+    constexpr int STEPS = 2 * T::DB;
+    constexpr int MPS = 2 * 16 / STEPS;  // max operations per step
+    bf16x8 va[STEPS];
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k)
+      va[k] = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + k / T::DB] + (k % T::DB) * 32 * T::VROW);
+    float mx[kQB] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
+#pragma unroll
+      for (int e = step * MPS; e < (step + 1) * MPS; ++e) mx[e / 16] = fmaxf(mx[e / 16], sb[e / 16][e % 16]);
+      const int gg = step / T::DB, db = step % T::DB;
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step], p[qb][gg], o[qb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) m_new[qb] = fmaxf(m_run[qb], max_halves(mx[qb]));
+  };
+
+  // Software pipeline over half tiles.  sa holds S^T of the current half
+  // (tile cur_t, half cur_j, LDS stage cur_i % 3), masked, with its reference
+  // max already settled.
+  int cur_t = next_tile(t_begin);
+  if (cur_t < t_end) {
+    int cur_j = 0, cur_i = 0;
+    issue_tile(cur_t, 0);
+    wait_dma_all();
     __syncthreads();
-    stage ^= 1;
-    t = tn;
+    int tn = next_tile(cur_t + 1);  // next tile of the sequence, already in flight
+    if (tn < t_end) issue_tile(tn, 1);
+    floatx16 sa[kQB];
+    float m_new[kQB];
+    qk_half(smem, 0, sa);
+    if (!tile_full(cur_t)) mask_half(cur_t, 0, sa);
+    max_half(sa, m_new);
+    rescale(m_new);
+    bf16x8 p[kQB][2];
+    while (true) {
+      int nt, nj, ni;
+      if (cur_j == 0) {
+        nt = cur_t;
+        nj = 1;
+        ni = cur_i;
+      } else {
+        if (tn >= t_end) break;
+        // the next half opens tile tn: publish it, then prefetch the one after
+        wait_dma_all();
+        __syncthreads();
+        const int tnn = next_tile(tn + 1);
+        if (tnn < t_end) issue_tile(tnn, (cur_i + 2) % kStages);
+        nt = tn;
+        nj = 0;
+        ni = cur_i + 1;
+        tn = tnn;
+      }
+      const char* st = smem + (cur_i % kStages) * T::STAGE;
+      const char* stn = smem + (ni % kStages) * T::STAGE;
+      floatx16 sb[kQB];
+      phase_a(stn, nj, sa, sb, p);
+      if (!tile_full(nt)) mask_half(nt, nj, sb);
+      phase_b(st, cur_j, p, sb, m_new);
+      rescale(m_new);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) sa[qb] = sb[qb];
+      cur_t = nt;
+      cur_j = nj;
+      cur_i = ni;
+    }
+    // the last half
+    exp_half(sa, p);
+    pv_half(smem + (cur_i % kStages) * T::STAGE, cur_j, p);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_v = l_tot > 0.f ? (m_run * a.scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (!qvalid) return;
-  if (a.splits == 1) {
-    __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(b) * a.Nq + qrow) * g.H + head) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float l_tot = sum_halves(l_run[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_v = l_tot > 0.f ? (m_run[qb] * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (!qvalid[qb]) continue;
+    if (a.splits == 1) {
+      __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(b) * a.Nq + qrow[qb]) * g.H + head) * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hl;
-        const __bf16 v0 = static_cast<__bf16>(o[db][4 * q4 + 0] * inv);
-        const __bf16 v1 = static_cast<__bf16>(o[db][4 * q4 + 1] * inv);
-        const __bf16 v2 = static_cast<__bf16>(o[db][4 * q4 + 2] * inv);
-        const __bf16 v3 = static_cast<__bf16>(o[db][4 * q4 + 3] * inv);
-        uint2 w;
-        w.x = uint32_t(__builtin_bit_cast(uint16_t, v0)) | (uint32_t(__builtin_bit_cast(uint16_t, v1)) << 16);
-        w.y = uint32_t(__builtin_bit_cast(uint16_t, v2)) | (uint32_t(__builtin_bit_cast(uint16_t, v3)) << 16);
-        *reinterpret_cast<uint2*>(op + d0) = w;
+      for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hl;
+          const __bf16 v0 = static_cast<__bf16>(o[qb][db][4 * q4 + 0] * inv);
+          const __bf16 v1 = static_cast<__bf16>(o[qb][db][4 * q4 + 1] * inv);
+          const __bf16 v2 = static_cast<__bf16>(o[qb][db][4 * q4 + 2] * inv);
+          const __bf16 v3 = static_cast<__bf16>(o[qb][db][4 * q4 + 3] * inv);
+          uint2 w;
+          w.x = uint32_t(__builtin_bit_cast(uint16_t, v0)) | (uint32_t(__builtin_bit_cast(uint16_t, v1)) << 16);
+          w.y = uint32_t(__builtin_bit_cast(uint16_t, v2)) | (uint32_t(__builtin_bit_cast(uint16_t, v3)) << 16);
+          *reinterpret_cast<uint2*>(op + d0) = w;
+        }
       }
-    }
-    if (a.lse && hl == 0) a.lse[(int64_t(b) * g.H + head) * a.Nq + qrow] = lse_v;
-  } else {
-    float* pp = a.part_o + (((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow) * D;
+      if (a.lse && hl == 0) a.lse[(int64_t(b) * g.H + head) * a.Nq + qrow[qb]] = lse_v;
+    } else {
+      float* pp = a.part_o + (((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow[qb]) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hl;
-        *reinterpret_cast<float4*>(pp + d0) = make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv,
-                                                           o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hl;
+          *reinterpret_cast<float4*>(pp + d0) =
+              make_float4(o[qb][db][4 * q4] * inv, o[qb][db][4 * q4 + 1] * inv, o[qb][db][4 * q4 + 2] * inv,
+                          o[qb][db][4 * q4 + 3] * inv);
+        }
       }
+      if (hl == 0) a.part_lse[((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow[qb]] = lse_v;
     }
-    if (hl == 0) a.part_lse[((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow] = lse_v;
   }
 }
 
@@ -547,12 +759,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
 }  // namespace
 
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_qtiles, a.g.H, a.g.B * a.splits);
+  dim3 grid(a.n_qtiles, a.g.H, a.g.B * a.splits);  // n_qtiles from attn_rows_per_workgroup()
   if (a.g.dtype == SCV_BF16) {
-    if (a.g.D == 128)
-      hipLaunchKernelGGL(chunk_attn_bf16_kernel<128>, grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(chunk_attn_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+    const bool f16 = a.g.qk_dtype == SCV_FP16;
+    if (a.g.D == 128) {
+      if (f16)
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, _Float16>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, __bf16>), grid, dim3(256), 0, s, a);
+    } else {
+      if (f16)
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, _Float16>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, __bf16>), grid, dim3(256), 0, s, a);
+    }
   } else {
     if (a.g.D == 128)
       hipLaunchKernelGGL(chunk_attn_f32_kernel<128>, grid, dim3(256), 0, s, a);

@@ -75,14 +75,8 @@ __global__ __launch_bounds__(256) void cache_reset_kernel(uint4* kv, int64_t n16
 }
 
 template <typename T>
-struct Vec16;  // 16 bytes of T
-template <>
-struct Vec16<float> {
-  static constexpr int N = 4;
-};
-template <>
-struct Vec16<__bf16> {
-  static constexpr int N = 8;
+struct Vec16 {  // elements of T in 16 bytes
+  static constexpr int N = 16 / int(sizeof(T));
 };
 
 template <typename T>
@@ -102,28 +96,33 @@ __device__ __forceinline__ void unpack16(const uint4 u, float* x) {
   }
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // round to nearest even through the native conversion
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
+// Two fp32 values rounded (to nearest even, native conversion) into the
+// 16-bit type T and packed.
+template <typename T>
+__device__ __forceinline__ uint32_t pack_x2(float lo, float hi) {
+  const T a = static_cast<T>(lo);
+  const T b = static_cast<T>(hi);
   return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+// fp32 values rounded to T, 16 bytes worth (4 fp32 or 8 16-bit values).
 template <typename T>
 __device__ __forceinline__ uint4 pack16(const float* x) {
   if constexpr (sizeof(T) == 4) {
     return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
   } else {
-    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                      pack_bf16x2(x[6], x[7]));
+    return make_uint4(pack_x2<T>(x[0], x[1]), pack_x2<T>(x[2], x[3]), pack_x2<T>(x[4], x[5]),
+                      pack_x2<T>(x[6], x[7]));
   }
 }
 
 constexpr int kTokTile = 64;
 
 // One workgroup: tokens [p0, p0+64) of frame f of stream b, one head.
-template <typename T, int D>
+// T: type of q, k, v inputs and cached values; QT: type of rotated q/k.
+template <typename T, typename QT, int D>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
+  static_assert(sizeof(T) == sizeof(QT), "rotated and input elements share a size");
   constexpr int EPV = Vec16<T>::N;      // elements per 16-byte vector
   constexpr int TPR = D / EPV;          // threads per token row
   constexpr int TPP = 256 / TPR;        // tokens per pass
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
         y[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
         y[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
       }
-      *reinterpret_cast<uint4*>(static_cast<T*>(a.q_out) + in_off) = pack16<T>(y);
+      *reinterpret_cast<uint4*>(static_cast<QT*>(a.q_out) + in_off) = pack16<QT>(y);
     }
     if (do_k && valid) {
       const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + in_off);
@@ -201,14 +200,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
           y[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
           y[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
         }
-        outv = pack16<T>(y);
+        outv = pack16<QT>(y);
       }
       if (to_cache) {
         const int64_t row = slot * g.slot_rows + p;
-        T* dst = static_cast<T*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + row) * D + dg * EPV;
+        QT* dst = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + row) * D + dg * EPV;
         *reinterpret_cast<uint4*>(dst) = outv;
       } else {
-        *reinterpret_cast<uint4*>(static_cast<T*>(a.k_out) + in_off) = outv;
+        *reinterpret_cast<uint4*>(static_cast<QT*>(a.k_out) + in_off) = outv;
       }
     }
     if (do_v) {
@@ -252,23 +251,28 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   if (to_cache && tile == 0 && head == 0 && threadIdx.x == 0) a.stamps[int64_t(b) * g.n_slots + slot] = gframe;
 }
 
-template <typename T, int D>
+template <typename T, typename QT, int D>
 hipError_t launch_rope_append_t(const RopeArgs& a, hipStream_t s) {
   const int tiles_per_frame = (a.g.P + kTokTile - 1) / kTokTile;
   dim3 grid(tiles_per_frame * a.g.H, a.n_frames, a.g.B);
-  hipLaunchKernelGGL((rope_append_kernel<T, D>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((rope_append_kernel<T, QT, D>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, typename QT>
+hipError_t launch_rope_append_d(const RopeArgs& a, hipStream_t s) {
+  if (a.g.D == 128) return launch_rope_append_t<T, QT, 128>(a, s);
+  return launch_rope_append_t<T, QT, 64>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s) {
   if (a.g.dtype == SCV_BF16) {
-    if (a.g.D == 128) return launch_rope_append_t<__bf16, 128>(a, s);
-    return launch_rope_append_t<__bf16, 64>(a, s);
+    if (a.g.qk_dtype == SCV_FP16) return launch_rope_append_d<__bf16, _Float16>(a, s);
+    return launch_rope_append_d<__bf16, __bf16>(a, s);
   }
-  if (a.g.D == 128) return launch_rope_append_t<float, 128>(a, s);
-  return launch_rope_append_t<float, 64>(a, s);
+  return launch_rope_append_d<float, float>(a, s);
 }
 
 hipError_t launch_rope_tables(const Geometry& g, const Omegas& om, const int64_t* t0, int32_t n_frames, float* out_t,

@@ -40,6 +40,11 @@ scv_status derive(const scv_config* c, scv::Geometry* g, scv_cache_layout* L, st
     *why = "dtype must be SCV_FP32 or SCV_BF16";
     return SCV_E_DTYPE;
   }
+  const int qk = c->qk_dtype == 0 ? c->dtype : c->qk_dtype;
+  if (!(qk == c->dtype || (qk == SCV_FP16 && c->dtype == SCV_BF16))) {
+    *why = "qk_dtype must be 0, equal to dtype, or SCV_FP16 with dtype SCV_BF16";
+    return SCV_E_DTYPE;
+  }
   if (c->head_dim != 64 && c->head_dim != 128) {
     *why = "head_dim must be 64 or 128";
     return SCV_E_DTYPE;
@@ -100,6 +105,7 @@ scv_status derive(const scv_config* c, scv::Geometry* g, scv_cache_layout* L, st
   g->rows = n_slots * g->slot_rows;
   g->rows_pad = int64_t(align_up(size_t(g->rows), scv::kKeyTile));
   g->dtype = c->dtype;
+  g->qk_dtype = qk;
   g->elem_bytes = c->dtype == SCV_BF16 ? 2 : 4;
   g->base = c->rope_base;
 
@@ -204,7 +210,8 @@ int resolve_splits(const scv_cache* c, int32_t n_frames, int32_t requested) {
   const int tiles = int(c->g.rows_pad / scv::kKeyTile);
   if (requested > 0) return std::max(1, std::min(std::min(requested, tiles), 64));
   const int64_t nq = int64_t(n_frames) * c->g.P;
-  const int64_t qtiles = (nq + 127) / 128;
+  const int rows = scv::attn_rows_per_workgroup(c->g);
+  const int64_t qtiles = (nq + rows - 1) / rows;
   const int64_t wgs = qtiles * c->g.H * c->g.B;
   const int cus = device_cu_count();
   if (wgs >= cus) return 1;
@@ -438,7 +445,7 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
     a.stamps = reinterpret_cast<const int64_t*>(c->base + c->lay.stamps_offset);
     a.n_frames = n_frames;
     a.Nq = n_frames * c->g.P;
-    a.n_qtiles = (a.Nq + 127) / 128;
+    a.n_qtiles = (a.Nq + scv::attn_rows_per_workgroup(c->g) - 1) / scv::attn_rows_per_workgroup(c->g);
     a.splits = splits;
     a.tiles_total = int32_t(c->g.rows_pad / scv::kKeyTile);
     a.tiles_per_split = (a.tiles_total + splits - 1) / splits;

@@ -16,6 +16,8 @@ constexpr int kMaxAxisPairs = 64;  // d_a / 2 <= head_dim / 2 <= 64
 constexpr int kMaxQueryChunks = 8;
 constexpr int kKeyTile = 64;       // rows per attention key tile
 constexpr int64_t kMaxTime = int64_t(1) << 40;
+constexpr int kAttnRowsBf16 = 256;  // query rows per attention workgroup (bf16)
+constexpr int kAttnRowsF32 = 128;   // query rows per attention workgroup (fp32)
 
 // Everything about a cache that kernels need, resolved once on the host.
 struct Geometry {
@@ -23,7 +25,8 @@ struct Geometry {
   int32_t grid_h, grid_w, P;
   int32_t S_f, W, C, k_max, R, n_slots;
   int64_t slot_rows, rows, rows_pad;
-  int32_t dtype;  // scv_dtype
+  int32_t dtype;     // scv_dtype of q, k, v, o and the cached values
+  int32_t qk_dtype;  // scv_dtype of rotated q/k and the cached keys
   int32_t elem_bytes;
   double base;
 };
@@ -85,6 +88,10 @@ struct MergeArgs {
   int32_t Nq;
   Geometry g;
 };
+
+inline int attn_rows_per_workgroup(const Geometry& g) {
+  return g.dtype == SCV_BF16 ? kAttnRowsBf16 : kAttnRowsF32;
+}
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);

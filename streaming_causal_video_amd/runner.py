@@ -34,11 +34,11 @@ class StreamRunner:
         nq = w.query_frames
         self.n_frames = nq
         shape = (w.batch, nq * w.tokens_per_frame, w.heads, w.head_dim)
-        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        tdt = self.cache.dtype
         self.q = to_device(G.frames_tensor(w, G.TENSOR_Q, w.t0, nq), w.dtype, device)
         self.k = to_device(G.frames_tensor(w, G.TENSOR_K, w.t0, nq), w.dtype, device)
         self.v = to_device(G.frames_tensor(w, G.TENSOR_V, w.t0, nq), w.dtype, device)
-        self.q_rot = torch.empty(shape, dtype=tdt, device=device)
+        self.q_rot = torch.empty(shape, dtype=self.cache.qk_dtype, device=device)
         self.o = torch.empty(shape, dtype=tdt, device=device)
         self.lse = torch.empty((w.batch, w.heads, nq * w.tokens_per_frame), dtype=torch.float32, device=device) \
             if with_lse else None

@@ -35,6 +35,7 @@ class Workload:
     t0: Tuple[int, ...]
     seed: int
     max_query_chunks: int = 1
+    qk_dtype: str = ""  # format of rotated q/k ("" = dtype, or "fp16")
     k_outlier_frac: float = 0.0
     k_outlier_scale: float = 1.0
     description: str = ""
@@ -116,7 +117,12 @@ WAN14B_480P = WAN13B_480P.with_(
     seed=4,
     k_outlier_frac=0.01,
     k_outlier_scale=30.0,
-    description="14B-shaped 480p layer: 40 heads, 1% of raw k entries scaled x30",
+    # bf16 rounding of the rotated q and k alone puts this workload's output
+    # 1.3e-2 (relative L2) from the exact result; fp16 rotated operands keep
+    # 3 more mantissa bits at the same MFMA rate (values stay far inside the
+    # fp16 range).  Inputs, cached values and the output stay bf16.
+    qk_dtype="fp16",
+    description="14B-shaped 480p layer: 40 heads, 1% of raw k entries scaled x30 (rotated q/k in fp16)",
 )
 
 WAN13B_720P = WAN13B_480P.with_(

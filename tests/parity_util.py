@@ -96,7 +96,7 @@ def check_rounding(name, got, ref, dtype):
     arithmetic), a much tighter check than the L2 bar for pure rotations."""
     # one rounding of the result, plus fp32 rounding of x*c and y*s, which
     # stays absolute when the two products cancel (inputs are O(1)..O(100))
-    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -22
+    rel = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 2.0 ** -22}[dtype]
     bound = rel * np.abs(ref) + 2.0 ** -20 * max(1.0, float(np.max(np.abs(ref))) / 4.0)
     bad = np.abs(got - ref) > bound
     assert not bad.any(), (name, int(bad.sum()), float(np.max(np.abs(got - ref))))

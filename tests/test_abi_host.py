@@ -62,6 +62,14 @@ def test_layout_of_workloads(lib):
         assert B.cache_bytes(cfg) == L.total_bytes
 
 
+def test_qk_fp16_layout_matches_bf16(lib):
+    kw = good_kwargs()
+    a = B.cache_layout(B.make_config(**kw))
+    kw["qk_dtype"] = "fp16"
+    b = B.cache_layout(B.make_config(**kw))
+    assert a.total_bytes == b.total_bytes and a.k_offset == b.k_offset and a.v_offset == b.v_offset
+
+
 def test_odd_grid_pads_slots(lib):
     cfg = B.make_config(batch=2, heads=3, head_dim=64, split=(24, 20, 20), base=1e4, grid_h=3, grid_w=5,
                         sink_frames=1, window_frames=3, chunk_frames=2, dtype="bf16")
@@ -80,6 +88,9 @@ BAD_CONFIGS = [
     ("grid", dict(grid_h=0), "SCV_E_INVALID"),
     ("slots", dict(window_frames=61), "SCV_E_INVALID"),
     ("chunks", dict(max_query_chunks=9), "SCV_E_INVALID"),
+    ("qk_fp16_with_fp32", dict(dtype="fp32", qk_dtype="fp16"), "SCV_E_DTYPE"),
+    ("qk_unknown", dict(qk_dtype=7), "SCV_E_DTYPE"),
+    ("qk_bf16_with_fp32", dict(dtype="fp32", qk_dtype="bf16"), "SCV_E_DTYPE"),
 ]
 
 

@@ -46,7 +46,15 @@ SMALL = [
     small("max-t0-bf16", t0=((1 << 40) - 2,), seed=111),
     small("long-tiles-bf16", heads=2, grid_h=20, grid_w=26, chunk_frames=2, window_frames=6, t0=(50,), seed=112),
     small("outliers-bf16", grid_h=6, grid_w=8, t0=(30,), k_outlier_frac=0.01, k_outlier_scale=30.0, seed=113),
+    small("outliers-qkfp16", grid_h=6, grid_w=8, t0=(30,), k_outlier_frac=0.01, k_outlier_scale=30.0, seed=114,
+          qk_dtype="fp16"),
+    small("qkfp16-d64-b2", batch=2, heads=3, head_dim=64, split=(24, 20, 20), grid_h=5, grid_w=6, t0=(17, 2),
+          qk_dtype="fp16", seed=115),
 ]
+
+
+def qk(w):
+    return w.qk_dtype or w.dtype
 
 
 def run_gpu(w, kv_splits=0, fused=True):
@@ -57,9 +65,7 @@ def run_gpu(w, kv_splits=0, fused=True):
     if fused:
         r.append()
     else:
-        q_rot = r.q.clone()
-        k_rot = r.k.clone()
-        r.cache.rope3d_apply(q_rot, k_rot, w.t0, r.n_frames)
+        q_rot, k_rot = r.cache.rope3d_apply(r.q.clone(), r.k.clone(), w.t0, r.n_frames)
         r.cache.kv_append_roll(k_rot, r.v, w.t0, r.n_frames)
         r.q_rot.copy_(q_rot)
     r.attend()
@@ -80,7 +86,7 @@ def check_cache_contents(r, oc, w, heads=None):
                 continue
             rows = slice(s * L.slot_rows, s * L.slot_rows + P)
             kg = to_np(v["k"][b, heads, rows, :]).transpose(1, 0, 2)
-            check_rounding(f"k slot {s}", kg, oc.k[b][s][:, heads], w.dtype)
+            check_rounding(f"k slot {s}", kg, oc.k[b][s][:, heads], qk(w))
             vg = to_np(v["v_t"][b, heads, :, rows]).transpose(2, 0, 1)
             assert np.array_equal(vg, oc.v[b][s][:, heads]), f"v slot {s} stream {b}"
 
@@ -130,7 +136,7 @@ def test_small_parity_full(w, gpu_lib):
     r = run_gpu(w)
     oc, q_rot = oracle_replay(w)
     check_values("q_rot", to_np(r.q_rot), q_rot, w.dtype)
-    check_rounding("q_rot", to_np(r.q_rot), q_rot, w.dtype)
+    check_rounding("q_rot", to_np(r.q_rot), q_rot, qk(w))
     check_cache_contents(r, oc, w)
     check_attention(r, oc, q_rot, w)
 
@@ -142,7 +148,7 @@ def test_workload_parity(w, gpu_lib):
     say(f"  gpu done (splits={r.splits}); oracle replay")
     oc, q_rot = oracle_replay(w)
     check_values("q_rot", to_np(r.q_rot), q_rot, w.dtype, per_axis0=True)
-    check_rounding("q_rot", to_np(r.q_rot), q_rot, w.dtype)
+    check_rounding("q_rot", to_np(r.q_rot), q_rot, qk(w))
     heads = sorted({0, w.heads // 2, w.heads - 1})
     check_cache_contents(r, oc, w, heads=heads)
     rows = None if w.query_rows <= 4096 and w.dtype == "fp32" else sample_rows(w.query_rows, w.seed)
@@ -171,7 +177,7 @@ def test_split_kv_720p(gpu_lib):
     check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, 7, n_random=96))
 
 
-@pytest.mark.parametrize("w", [SMALL[0], SMALL[3], SMALL[4]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[3], SMALL[4], SMALL[-1]], ids=lambda w: w.name)
 def test_unfused_equals_fused(w, gpu_lib):
     import torch
 
