@@ -136,18 +136,21 @@ __device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int 
 // row index swapped) so that the S^T accumulator of lane half h holds, per
 // 16-key group, exactly keys 8h..8h+7 of that group: P^T then pairs with
 // V^T read in natural key order (one 16-byte read per lane).  Both tiles
-// carry an XOR swizzle of 16-byte chunks against LDS bank conflicts.
+// carry an XOR swizzle of 16-byte chunks that puts any 16 consecutive lanes
+// of a fragment read on distinct banks (64 banks of 4 bytes).
 // Softmax rescaling is lazy: the reference max moves only when a row's
 // max grows by more than 2^8 (so exponentials stay <= 256).
 // ---------------------------------------------------------------------------
 // Direct global -> LDS load of 16 bytes per lane: lane l writes LDS byte
-// address lds_base + 16*l (lds_base wave-uniform, via M0); the source address
-// is the lane's own.  Issued through inline assembly so that the compiler does
+// address lds_base + 16*l (lds_base wave-uniform, via M0) from base + voff
+// (base wave-uniform in SGPRs, voff the lane's unsigned 32-bit offset, kept
+// in a register that is never rewritten, so issuing the next load never
+// waits for this one to read its address).  Issued through inline assembly so that the compiler does
 // not guard later LDS reads of other buffers with waits on these loads; the
 // kernel waits for them itself (vmcnt) before the barrier that publishes a
 // tile.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_base), "v"(src) : "m0", "memory");
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(voff), "s"(base) : "m0", "memory");
 }
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -192,6 +195,58 @@ struct Bf16Tile {
   static constexpr int K_ROWS_PER_DMA = 1024 / KROW;
   static constexpr int KS = D / 16;              // k-steps of QK^T
   static constexpr int DB = D / 32;              // 32-row blocks of O^T
+  // chunk swizzle of LDS row r: rows of 256 bytes span all 64 banks, rows of
+  // 128 bytes half of them (so row pairs share a swizzle value)
+  static __device__ __forceinline__ int kswz(int r) { return KROW == 256 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
+};
+
+// Division-free walk over the key tiles of a split: for the tile under the
+// cursor it tracks the frame slots of its first and last row, so that the
+// visibility of each tile costs a few scalar operations.
+struct TileWalk {
+  int t, t_end;
+  int r0, slo, slo_end, shi, shi_end;  // first row; slot of first/last row; row after each slot
+
+  __device__ __forceinline__ void init(const Geometry& g, int t_begin, int t_end_) {
+    t = t_begin;
+    t_end = t_end_;
+    r0 = t * kKeyTile;
+    const int sr = int(g.slot_rows);
+    slo = r0 / sr;
+    slo_end = (slo + 1) * sr;
+    const int r1 = min(r0 + kKeyTile - 1, int(g.rows) - 1);
+    shi = r1 / sr;
+    shi_end = (shi + 1) * sr;
+  }
+  __device__ __forceinline__ void step(const Geometry& g) {
+    const int sr = int(g.slot_rows);
+    ++t;
+    r0 += kKeyTile;
+    while (r0 >= slo_end) {
+      ++slo;
+      slo_end += sr;
+    }
+    const int r1 = min(r0 + kKeyTile - 1, int(g.rows) - 1);
+    while (r1 >= shi_end) {
+      ++shi;
+      shi_end += sr;
+    }
+  }
+  __device__ __forceinline__ uint64_t bits(const Geometry& g) const {
+    if (r0 >= int(g.rows)) return 0;
+    const uint64_t hi = shi >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (shi + 1)) - 1);
+    return hi & ~((uint64_t(1) << slo) - 1);
+  }
+  // advance to the next tile some query of the workgroup may see (from the
+  // cursor itself when `first`); returns t_end when there is none
+  __device__ __forceinline__ int next(const Geometry& g, const Visibility& v, bool first, bool* full) {
+    if (!first) step(g);
+    while (t < t_end && (bits(g) & v.any) == 0) step(g);
+    if (t >= t_end) return t_end;
+    *full = ((bits(g) & ~v.all) == 0) && (r0 + kKeyTile <= int(g.rows)) && (g.slot_rows == g.P);
+    return t;
+  }
 };
 
 template <int D, typename QKT>
@@ -228,30 +283,34 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, a.tiles_total);
-  auto next_tile = [&](int t) {
-    while (t < t_end && (tile_slot_bits(g, t) & vis.any) == 0) ++t;
-    return t;
-  };
 
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
   const char* kbase = static_cast<const char*>(a.cache_k) + (int64_t(b) * g.H + head) * g.rows_pad * T::KROW;
-  const char* vbase = static_cast<const char*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad * 2;
+  const int64_t vpitch = g.rows_pad * 2;  // bytes per V^T row in the cache
+  const char* vbase = static_cast<const char*>(a.cache_v) + (int64_t(b) * g.H + head) * D * vpitch;
+  // per-lane source offsets inside a tile (loop invariant); LDS is filled
+  // linearly and the swizzle is applied on the source side
+  uint32_t kvo[T::K_DMA], vvo[T::V_DMA];
+#pragma unroll
+  for (int i = 0; i < T::K_DMA; ++i) {
+    const int r = (wave * T::K_DMA + i) * T::K_ROWS_PER_DMA + lane / T::CH;  // LDS row
+    kvo[i] = uint32_t(kperm(r) * T::KROW + (((lane % T::CH) ^ T::kswz(r)) * 16));
+  }
+#pragma unroll
+  for (int i = 0; i < T::V_DMA; ++i) {
+    const int r = (wave * T::V_DMA + i) * 8 + (lane >> 3);  // d row
+    vvo[i] = uint32_t((lane >> 3) * vpitch + (((lane & 7) ^ T::vswz(r)) * 16));
+  }
   auto issue_tile = [&](int t, int stg) {
     const int64_t r0 = int64_t(t) * kKeyTile;
-    const uint32_t kdst = lds0 + uint32_t(stg * T::STAGE);
+    const uint32_t dst = lds0 + uint32_t(stg * T::STAGE);
 #pragma unroll
-    for (int i = 0; i < T::K_DMA; ++i) {
-      const int n = wave * T::K_DMA + i;
-      const int r = n * T::K_ROWS_PER_DMA + lane / T::CH;  // LDS row
-      const int gc = (lane % T::CH) ^ (r & (T::CH - 1));    // source chunk
-      dma16(kbase + (r0 + kperm(r)) * T::KROW + gc * 16, kdst + uint32_t(n * 1024));
-    }
+    for (int i = 0; i < T::K_DMA; ++i)
+      dma16(kbase + r0 * T::KROW, kvo[i], dst + uint32_t((wave * T::K_DMA + i) * 1024));
 #pragma unroll
     for (int i = 0; i < T::V_DMA; ++i) {
       const int n = wave * T::V_DMA + i;
-      const int r = n * 8 + (lane >> 3);  // d row
-      const int gc = (lane & 7) ^ (r & 7);
-      dma16(vbase + int64_t(r) * g.rows_pad * 2 + r0 * 2 + gc * 16, kdst + uint32_t(T::KBYTES + n * 1024));
+      dma16(vbase + int64_t(n * 8) * vpitch + r0 * 2, vvo[i], dst + uint32_t(T::KBYTES + n * 1024));
     }
   };
 
@@ -271,10 +330,10 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   // loop-invariant LDS byte offsets of this lane's K and V^T fragments
   int koff[T::KS];
 #pragma unroll
-  for (int kk = 0; kk < T::KS; ++kk) koff[kk] = l32 * T::KROW + (((2 * kk + hl) ^ (l32 & (T::CH - 1))) * 16);
+  for (int kk = 0; kk < T::KS; ++kk) koff[kk] = l32 * T::KROW + (((2 * kk + hl) ^ T::kswz(l32)) * 16);
   int voff[4];
 #pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) voff[g4] = T::KBYTES + l32 * T::VROW + (((2 * g4 + hl) ^ (l32 & 7)) * 16);
+  for (int g4 = 0; g4 < 4; ++g4) voff[g4] = T::KBYTES + l32 * T::VROW + (((2 * g4 + hl) ^ T::vswz(l32)) * 16);
 
   floatx16 o[kQB][T::DB];
 #pragma unroll
@@ -290,6 +349,8 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   }
   const float c = a.scale_log2;
   const float lazy = 8.f / c;  // raw-score growth that forces a rescale (2^8)
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // S^T of one half tile (32 keys = LDS rows 32j .. 32j+31) for both blocks
   auto qk_half = [&](const char* st, int j, floatx16* s) {
@@ -312,37 +373,7 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       for (int qb = 0; qb < kQB; ++qb) s[qb][i] = key_visible(g, mine[qb], key) ? s[qb][i] : -INFINITY;
     }
   };
-  auto tile_full = [&](int t) {
-    const int64_t r0 = int64_t(t) * kKeyTile;
-    return ((tile_slot_bits(g, t) & ~vis.all) == 0) && (r0 + kKeyTile <= g.rows) && (g.slot_rows == g.P);
-  };
-  // P^T (bf16) of a half for both blocks; accumulates the row sums
-  auto exp_half = [&](const floatx16* s, bf16x8 (*p)[2]) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float rs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(__builtin_fmaf(s[qb][i], c, -msc[qb]));
-        rs += e;
-        p[qb][i / 8][i % 8] = static_cast<__bf16>(e);
-      }
-      l_run[qb] += rs;
-    }
-  };
-  // O^T += V^T P^T for the two 16-key groups of half j
-  auto pv_half = [&](const char* st, int j, bf16x8 (*p)[2]) {
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[qb][gg], o[qb][db], 0, 0, 0);
-      }
-  };
-  // row max of a half; returns the candidate new maxima
+  // row max of a half (both blocks) against the running reference max
   auto max_half = [&](const floatx16* s, float* m_new) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -366,11 +397,22 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       msc[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
     }
   };
-
-  // Phase A: S^T of the next half (tile stn, half nj) on the MFMA pipe,
+  // P^T of a half (bf16) from its S^T; row sums over the rounded values
+  auto exp_step = [&](const floatx16* sa, bf16x8 (*p)[2], float* rs, int e0, int n) {
+#pragma unroll
+    for (int e = e0; e < e0 + n; ++e) {
+      const int qb = e / 16, i = e % 16;
+      p[qb][i / 8][i % 8] = static_cast<__bf16>(fast_exp2(__builtin_fmaf(sa[qb][i], c, -msc[qb])));
+      if (i % 2 == 1) {
+        const bf16x2 pr = {p[qb][i / 8][i % 8 - 1], p[qb][i / 8][i % 8]};
+        rs[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs[qb], false);
+      }
+    }
+  };
+  // Phase A: S^T of the next half (stage stn, half nj) runs on the MFMA pipe
   // interleaved step by step with the exponentials of the current half
-  // (sa -> P^T in p, row sums into l_run).  Source order is kept by
-  // sched_barrier so each step's VALU work sits in the shadow of its MFMAs.
+  // (sa -> p).  sched_barrier keeps
+  // the source order, pin() keeps the exponentials in this block.
   auto phase_a = [&](const char* stn, int nj, const floatx16* sa, floatx16* sb, bf16x8 (*p)[2]) {
     constexpr int EPS = 2 * 16 / T::KS;  // exponentials per step
     qk8 kf[T::KS];
@@ -381,15 +423,10 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     float rs[kQB] = {0.f, 0.f};
 #pragma unroll
     for (int step = 0; step < T::KS; ++step) {
-#pragma unroll
-      for (int e = step * EPS; e < (step + 1) * EPS; ++e) {
-        const int qb = e / 16, i = e % 16;
-        const float x = fast_exp2(__builtin_fmaf(sa[qb][i], c, -msc[qb]));
-        rs[qb] += x;
-        p[qb][i / 8][i % 8] = static_cast<__bf16>(x);
-      }
+      exp_step(sa, p, rs, step * EPS, EPS);
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) sb[qb] = mfma_32x32x16(kf[step], qf[qb][step], sb[qb]);
+
       if ((step + 1) * EPS % 8 == 0) pin(p[((step + 1) * EPS - 1) / 16][(((step + 1) * EPS - 1) % 16) / 8]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -399,8 +436,8 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       l_run[qb] += rs[qb];
     }
   };
-  // Phase B: O^T += V^T P^T of the current half (tile st, half j) on the MFMA
-  // pipe, interleaved with the row max of the next half (sb -> m_new).
+  // Phase B: O^T += V^T P^T of the current half on the MFMA pipe,
+  // interleaved with the row max of the next half (sb -> m_new).
   auto phase_b = [&](const char* st, int j, bf16x8 (*p)[2], const floatx16* sb, float* m_new) {
     constexpr int STEPS = 2 * T::DB;
     constexpr int MPS = 2 * 16 / STEPS;  // max operations per step
@@ -422,59 +459,104 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) m_new[qb] = fmaxf(m_run[qb], max_halves(mx[qb]));
   };
+  // the last half: exponentials, then P V
+  auto finish_half = [&](const char* st, int j, const floatx16* sa) {
+    bf16x8 p[kQB][2];
+    float rs[kQB] = {0.f, 0.f};
+    exp_step(sa, p, rs, 0, 2 * 16);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += rs[qb];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[qb][gg], o[qb][db], 0, 0, 0);
+      }
+  };
 
-  // Software pipeline over half tiles.  sa holds S^T of the current half
-  // (tile cur_t, half cur_j, LDS stage cur_i % 3), masked, with its reference
-  // max already settled.
-  int cur_t = next_tile(t_begin);
-  if (cur_t < t_end) {
-    int cur_j = 0, cur_i = 0;
-    issue_tile(cur_t, 0);
+  // Pass 1 -- the fully visible tiles (all of them in steady state), through
+  // a software pipeline over half tiles, two halves per loop trip: S^T of the
+  // next half is computed while the current half is finished.  Tile i of the
+  // pass lives in LDS stage i % 3; tiles are prefetched two ahead.  Online
+  // softmax does not depend on key order, so the partially visible tiles
+  // are taken afterwards (pass 2) and this loop carries no masking code.
+  TileWalk walk;
+  walk.init(g, t_begin, t_end);
+  auto next_full = [&](bool first) {
+    bool full = false;
+    int t = walk.next(g, vis, first, &full);
+    while (t < t_end && !full) t = walk.next(g, vis, false, &full);
+    return t;
+  };
+  int t = next_full(true);
+  if (t < t_end) {
+    issue_tile(t, 0);
     wait_dma_all();
     __syncthreads();
-    int tn = next_tile(cur_t + 1);  // next tile of the sequence, already in flight
+    int tn = next_full(false);
     if (tn < t_end) issue_tile(tn, 1);
-    floatx16 sa[kQB];
+    int ti = 0;
+    floatx16 sa[kQB], sb[kQB];
     float m_new[kQB];
+    bf16x8 p[kQB][2];
     qk_half(smem, 0, sa);
-    if (!tile_full(cur_t)) mask_half(cur_t, 0, sa);
     max_half(sa, m_new);
     rescale(m_new);
-    bf16x8 p[kQB][2];
     while (true) {
-      int nt, nj, ni;
-      if (cur_j == 0) {
-        nt = cur_t;
-        nj = 1;
-        ni = cur_i;
-      } else {
-        if (tn >= t_end) break;
-        // the next half opens tile tn: publish it, then prefetch the one after
-        wait_dma_all();
-        __syncthreads();
-        const int tnn = next_tile(tn + 1);
-        if (tnn < t_end) issue_tile(tnn, (cur_i + 2) % kStages);
-        nt = tn;
-        nj = 0;
-        ni = cur_i + 1;
-        tn = tnn;
-      }
-      const char* st = smem + (cur_i % kStages) * T::STAGE;
-      const char* stn = smem + (ni % kStages) * T::STAGE;
-      floatx16 sb[kQB];
-      phase_a(stn, nj, sa, sb, p);
-      if (!tile_full(nt)) mask_half(nt, nj, sb);
-      phase_b(st, cur_j, p, sb, m_new);
+      const char* st = smem + (ti % kStages) * T::STAGE;
+      // half 0 of tile t (sa); the next half is half 1 of the same tile
+      phase_a(st, 1, sa, sb, p);
+      phase_b(st, 0, p, sb, m_new);
       rescale(m_new);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) sa[qb] = sb[qb];
-      cur_t = nt;
-      cur_j = nj;
-      cur_i = ni;
+      // half 1 of tile t (sb); the next half opens tile tn
+      if (tn >= t_end) {
+        finish_half(st, 1, sb);
+        break;
+      }
+      wait_dma_all();  // tile tn has landed (for this wave) ...
+      __syncthreads();  // ... and for every wave; tile ti-1's stage is free
+      const int tnn = next_full(false);
+      if (tnn < t_end) issue_tile(tnn, (ti + 2) % kStages);
+      const char* stn = smem + ((ti + 1) % kStages) * T::STAGE;
+      phase_a(stn, 0, sb, sa, p);
+      phase_b(st, 1, p, sa, m_new);
+      rescale(m_new);
+      t = tn;
+      tn = tnn;
+      ++ti;
     }
-    // the last half
-    exp_half(sa, p);
-    pv_half(smem + (cur_i % kStages) * T::STAGE, cur_j, p);
+  }
+
+  // Pass 2 -- partially visible tiles (warm-up, slot padding, the row tail),
+  // one at a time with per-key masks.
+  {
+    TileWalk pw;
+    pw.init(g, t_begin, t_end);
+    bool first = true;
+    while (true) {
+      bool full = true;
+      int tp = pw.next(g, vis, first, &full);
+      first = false;
+      while (tp < t_end && full) tp = pw.next(g, vis, false, &full);
+      if (tp >= t_end) break;
+      __syncthreads();  // every wave is done with stage 0
+      issue_tile(tp, 0);
+      wait_dma_all();
+      __syncthreads();
+#pragma unroll 1
+      for (int j = 0; j < 2; ++j) {
+        floatx16 s2[kQB];
+        float m2[kQB];
+        qk_half(smem, j, s2);
+        mask_half(tp, j, s2);
+        max_half(s2, m2);
+        rescale(m2);
+        finish_half(smem, j, s2);
+      }
+    }
   }
 
 #pragma unroll
