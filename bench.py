@@ -30,6 +30,40 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch of the attention kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE counter runs scaled by the same counters on a plain copy of
+# known size (bench.py --calibrate-copy).  Valid only for the kernel source
+# they were taken on: any other source hash reports null.
+MEASURED_TRAFFIC = {
+    # profiles/chunk_attn_wan13b_480p.md
+    "wan1.3b-480p": {"source": "0c717171f7c99756", "kv_splits": 1, "bytes_per_launch": 1256249910},
+}
+KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def calibrate_copy(nbytes):
+    """A plain device-to-device copy of nbytes (read nbytes, write nbytes),
+    repeated 5 times: the reference for scaling the HBM byte counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 5}), flush=True)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -107,12 +141,18 @@ def main():
     ap.add_argument("--workload", default="wan1.3b-480p")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this path "
               "is a design note, not a run.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
 
@@ -155,6 +195,10 @@ def main():
     eb = 2 if w.dtype == "bf16" else 4
     append_bytes = 6 * w.batch * w.query_rows * w.heads * w.head_dim * eb
     peak = PEAK_TFLOPS[w.dtype]
+    m = MEASURED_TRAFFIC.get(w.name)
+    traffic = None
+    if m and m["source"] == kernel_source_hash() and m["kv_splits"] == r.splits:
+        traffic = m["bytes_per_launch"]
     out = {
         "metric": "chunk-attn TFLOP/s (% MFMA bf16 peak) + latent frames/s, 1.3B-shape 480p",
         "value": step_tflops,
@@ -191,9 +235,11 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": attn_tflops / peak,
-            "traffic": None,
+            "traffic": traffic,
         },
     }
+    if r.splits > 1:
+        out["attn_ms_includes_merge"] = True
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -214,10 +214,25 @@ int resolve_splits(const scv_cache* c, int32_t n_frames, int32_t requested) {
   const int64_t qtiles = (nq + rows - 1) / rows;
   const int64_t wgs = qtiles * c->g.H * c->g.B;
   const int cus = device_cu_count();
-  if (wgs >= cus) return 1;
-  int s = int((2 * int64_t(cus) + wgs - 1) / wgs);
-  s = std::min(s, std::max(1, tiles / 8));
-  return std::max(1, std::min(s, 16));
+  // Estimated makespan in units of one workgroup-tile: rounds of workgroups
+  // over the compute units, each round as long as one split's key tiles
+  // plus a fixed start/drain cost of 3 tiles; with splits, the fp32
+  // partials are written and merged (their HBM bytes at ~24 MB per unit,
+  // plus 2 units for the extra launch).
+  const double rows_total = double(nq) * c->g.H * c->g.B;
+  double best = 0.0;
+  int best_s = 1;
+  for (int s = 1; s <= std::min(64, tiles); ++s) {
+    const int64_t per = (tiles + s - 1) / s;
+    const int64_t rounds = (wgs * s + cus - 1) / cus;
+    double cost = double(rounds) * double(per + 3);
+    if (s > 1) cost += 2.0 + 2.0 * rows_total * s * (4.0 * c->g.D + 4.0) / 24e6;
+    if (s == 1 || cost < best) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  return best_s;
 }
 
 size_t workspace_bytes(const scv_cache* c, int32_t n_frames, int splits) {
