@@ -128,16 +128,23 @@ __device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int 
 // bf16 inputs, fp32 accumulation; QKT = format of the rotated q/k operands
 // (bf16, or fp16 for 3 more mantissa bits at the same MFMA rate).
 //
-// One wave owns 64 query rows as two 32-row blocks, so every K or V^T
-// fragment read from LDS feeds two MFMAs; four waves (256 rows) share each
-// 64-key tile.  Tiles are moved global -> LDS by the 16-byte direct loads
-// of gfx950 (no VGPR staging), double-buffered, one barrier per tile.
-// In LDS, K rows are permuted inside each 16-row group (bits 2 and 3 of the
-// row index swapped) so that the S^T accumulator of lane half h holds, per
-// 16-key group, exactly keys 8h..8h+7 of that group: P^T then pairs with
-// V^T read in natural key order (one 16-byte read per lane).  Both tiles
-// carry an XOR swizzle of 16-byte chunks that puts any 16 consecutive lanes
-// of a fragment read on distinct banks (64 banks of 4 bytes).
+// Workgroup = 8 waves = 256 query rows of one (stream, head[, key split]);
+// each wave owns 32 query rows for the whole key loop, so a wave's S^T,
+// P^T, Q and O^T all stay in VGPRs.  Waves w and w + 4 share a SIMD and run
+// the same per-tile work in opposite order ("ping-pong"): waves 0-3 do
+// their MFMA phase (P V of the previous tile, then QK^T of this tile) and
+// then their softmax phase; waves 4-7 do the softmax of the previous tile
+// first.  While one wave of a SIMD is in its softmax (VALU), the other keeps
+// the matrix core busy.
+// Tiles of 64 keys move global -> LDS through the 16-byte direct loads of
+// gfx950 (no VGPR staging) into a ring of 4 stages, two tiles ahead of use,
+// with one barrier per tile.  In LDS, K rows are permuted inside each 16-row
+// group (bits 2 and 3 of the row index swapped) so that the S^T accumulator
+// of lane half h holds, per 16-key group, exactly keys 8h..8h+7 of that
+// group: P^T then pairs with V^T read in natural key order (one 16-byte read
+// per lane).  Both tiles carry an XOR swizzle of 16-byte chunks that puts
+// any 16 consecutive lanes of a fragment read on distinct banks (64 banks
+// of 4 bytes).
 // Softmax rescaling is lazy: the reference max moves only when a row's
 // max grows by more than 2^8 (so exponentials stay <= 256).
 // ---------------------------------------------------------------------------
@@ -145,14 +152,18 @@ __device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int 
 // address lds_base + 16*l (lds_base wave-uniform, via M0) from base + voff
 // (base wave-uniform in SGPRs, voff the lane's unsigned 32-bit offset, kept
 // in a register that is never rewritten, so issuing the next load never
-// waits for this one to read its address).  Issued through inline assembly so that the compiler does
-// not guard later LDS reads of other buffers with waits on these loads; the
-// kernel waits for them itself (vmcnt) before the barrier that publishes a
-// tile.
+// waits for this one to read its address).  Issued through inline assembly
+// so that the compiler does not guard later LDS reads of other buffers with
+// waits on these loads; the kernel waits for them itself (vmcnt) before the
+// barrier that publishes a tile.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(voff), "s"(base) : "m0", "memory");
 }
-__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 
 // max / sum of x over lanes l and l ^ 32 (one v_permlane32_swap)
 __device__ __forceinline__ float max_halves(float x) {
@@ -164,23 +175,14 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Empty asm that claims to modify a value: keeps the computation of x at this
-// point in the program (the optimizer may otherwise sink it past a branch to
-// its first use, out of the block whose MFMAs it is meant to overlap).
-__device__ __forceinline__ void pin(bf16x8& x) {
-  uint4 u = __builtin_bit_cast(uint4, x);
-  asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-  x = __builtin_bit_cast(bf16x8, u);
-}
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-
 // LDS row r of a K tile holds key row kperm(r) of the tile.
 __device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-constexpr int kQB = 2;                        // 32-query blocks per wave
-constexpr int kRowsBf16 = 32 * kQB * kWaves;  // 256 query rows per workgroup
+constexpr int kPPWaves = 8;                  // waves per workgroup (2 per SIMD)
+constexpr int kRowsBf16 = 32 * kPPWaves;     // 256 query rows per workgroup
 static_assert(kRowsBf16 == kAttnRowsBf16, "host and kernel agree on the query tile");
-constexpr int kStages = 3;                    // LDS tiles: consumed, landing, loading
+constexpr int kStages = 4;                   // LDS tile ring
+constexpr int kDmaWaves = 4;                 // waves 0-3 move the tiles
 
 template <int D>
 struct Bf16Tile {
@@ -190,8 +192,9 @@ struct Bf16Tile {
   static constexpr int VROW = kKeyTile * 2;      // bytes per V^T row (64 keys)
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int K_DMA = KBYTES / 1024 / kWaves;  // 1 KB loads per wave
-  static constexpr int V_DMA = VBYTES / 1024 / kWaves;
+  static constexpr int K_DMA = KBYTES / 1024 / kDmaWaves;  // 1 KB loads per loading wave
+  static constexpr int V_DMA = VBYTES / 1024 / kDmaWaves;
+  static constexpr int DMA = K_DMA + V_DMA;      // loads per loading wave per tile
   static constexpr int K_ROWS_PER_DMA = 1024 / KROW;
   static constexpr int KS = D / 16;              // k-steps of QK^T
   static constexpr int DB = D / 32;              // 32-row blocks of O^T
@@ -250,10 +253,11 @@ struct TileWalk {
 };
 
 template <int D, typename QKT>
-__global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   typedef typename Vec8<QKT>::type qk8;
   typedef Bf16Tile<D> T;
   static_assert(T::K_DMA >= 1 && T::V_DMA >= 1, "tile sizes");
+  constexpr int KS = T::KS, DB = T::DB;
 
   __shared__ __attribute__((aligned(1024))) char smem[kStages * T::STAGE];
   __shared__ uint64_t vis_mask[kMaxQueryChunks];
@@ -261,44 +265,36 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < 4;  // MFMA phase first
   const int hl = lane >> 5, l32 = lane & 31;
   const int qtile = blockIdx.x, head = blockIdx.y;
   const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
-  int qrow[kQB];
-  bool qvalid[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    qrow[qb] = qtile * kRowsBf16 + wave * 64 + qb * 32 + l32;
-    qvalid[qb] = qrow[qb] < a.Nq;
-  }
+  const int qrow = qtile * kRowsBf16 + wave * 32 + l32;
+  const bool qvalid = qrow < a.Nq;
 
-  const Visibility vis = compute_visibility<kRowsBf16>(a, b, qtile, qrow[0], qvalid[0], vis_mask);
-  uint64_t mine[kQB];
-  {
-    const int rows_per_chunk = g.P * g.C;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-      mine[qb] = vis_mask[qvalid[qb] ? qrow[qb] / rows_per_chunk : (qtile * kRowsBf16) / rows_per_chunk];
-  }
+  const Visibility vis = compute_visibility<kRowsBf16>(a, b, qtile, qrow, qvalid, vis_mask);
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, a.tiles_total);
 
+  // ---- global -> LDS tile copies ----
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
   const char* kbase = static_cast<const char*>(a.cache_k) + (int64_t(b) * g.H + head) * g.rows_pad * T::KROW;
   const int64_t vpitch = g.rows_pad * 2;  // bytes per V^T row in the cache
   const char* vbase = static_cast<const char*>(a.cache_v) + (int64_t(b) * g.H + head) * D * vpitch;
   // per-lane source offsets inside a tile (loop invariant); LDS is filled
   // linearly and the swizzle is applied on the source side
+  // (only waves 0 .. kDmaWaves-1 load; dw is their index)
+  const int dw = wave & (kDmaWaves - 1);
   uint32_t kvo[T::K_DMA], vvo[T::V_DMA];
 #pragma unroll
   for (int i = 0; i < T::K_DMA; ++i) {
-    const int r = (wave * T::K_DMA + i) * T::K_ROWS_PER_DMA + lane / T::CH;  // LDS row
+    const int r = (dw * T::K_DMA + i) * T::K_ROWS_PER_DMA + lane / T::CH;  // LDS row
     kvo[i] = uint32_t(kperm(r) * T::KROW + (((lane % T::CH) ^ T::kswz(r)) * 16));
   }
 #pragma unroll
   for (int i = 0; i < T::V_DMA; ++i) {
-    const int r = (wave * T::V_DMA + i) * 8 + (lane >> 3);  // d row
+    const int r = (dw * T::V_DMA + i) * 8 + (lane >> 3);  // d row
     vvo[i] = uint32_t((lane >> 3) * vpitch + (((lane & 7) ^ T::vswz(r)) * 16));
   }
   auto issue_tile = [&](int t, int stg) {
@@ -306,233 +302,214 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     const uint32_t dst = lds0 + uint32_t(stg * T::STAGE);
 #pragma unroll
     for (int i = 0; i < T::K_DMA; ++i)
-      dma16(kbase + r0 * T::KROW, kvo[i], dst + uint32_t((wave * T::K_DMA + i) * 1024));
+      dma16(kbase + r0 * T::KROW, kvo[i], dst + uint32_t((dw * T::K_DMA + i) * 1024));
 #pragma unroll
     for (int i = 0; i < T::V_DMA; ++i) {
-      const int n = wave * T::V_DMA + i;
+      const int n = dw * T::V_DMA + i;
       dma16(vbase + int64_t(n * 8) * vpitch + r0 * 2, vvo[i], dst + uint32_t(T::KBYTES + n * 1024));
     }
   };
 
-  // Q^T operands: lane (l32, hl) holds q[qrow][16*kk + 8*hl .. +8].
-  qk8 qf[kQB][T::KS];
+  // Q^T operand: lane (l32, hl) holds q[qrow][16*kk + 8*hl .. +8].
+  qk8 qf[KS];
+  {
+    const QKT* qp =
+        static_cast<const QKT*>(a.q) + ((int64_t(b) * a.Nq + (qvalid ? qrow : 0)) * g.H + head) * D + 8 * hl;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const QKT* qp = static_cast<const QKT*>(a.q) +
-                    ((int64_t(b) * a.Nq + (qvalid[qb] ? qrow[qb] : 0)) * g.H + head) * D + 8 * hl;
-#pragma unroll
-    for (int kk = 0; kk < T::KS; ++kk) {
-      const uint4 u = qvalid[qb] ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-      qf[qb][kk] = __builtin_bit_cast(qk8, u);
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      qf[kk] = __builtin_bit_cast(qk8, u);
     }
   }
 
   // loop-invariant LDS byte offsets of this lane's K and V^T fragments
-  int koff[T::KS];
+  int koff[KS];
 #pragma unroll
-  for (int kk = 0; kk < T::KS; ++kk) koff[kk] = l32 * T::KROW + (((2 * kk + hl) ^ T::kswz(l32)) * 16);
+  for (int kk = 0; kk < KS; ++kk) koff[kk] = l32 * T::KROW + (((2 * kk + hl) ^ T::kswz(l32)) * 16);
   int voff[4];
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) voff[g4] = T::KBYTES + l32 * T::VROW + (((2 * g4 + hl) ^ T::vswz(l32)) * 16);
 
-  floatx16 o[kQB][T::DB];
+  floatx16 o[DB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) o[qb][db] = floatx16{};
-  float m_run[kQB], l_run[kQB], msc[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-    msc[qb] = 0.f;
-  }
+  for (int db = 0; db < DB; ++db) o[db] = floatx16{};
+  float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
   const float lazy = 8.f / c;  // raw-score growth that forces a rescale (2^8)
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  // S^T of one half tile (32 keys = LDS rows 32j .. 32j+31) for both blocks
-  auto qk_half = [&](const char* st, int j, floatx16* s) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) s[qb] = floatx16{};
-#pragma unroll
-    for (int kk = 0; kk < T::KS; ++kk) {
-      const qk8 kf = *reinterpret_cast<const qk8*>(st + koff[kk] + j * 32 * T::KROW);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) s[qb] = mfma_32x32x16(kf, qf[qb][kk], s[qb]);
-    }
-  };
-  // element i of a half's accumulator in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4)
-  auto mask_half = [&](int t, int j, floatx16* s) {
-    const int r0 = t * kKeyTile + 32 * j;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = r0 + kperm(8 * (i / 4) + 4 * hl + (i & 3));
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) s[qb][i] = key_visible(g, mine[qb], key) ? s[qb][i] : -INFINITY;
-    }
-  };
-  // row max of a half (both blocks) against the running reference max
-  auto max_half = [&](const floatx16* s, float* m_new) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[qb][i], s[qb][i + 1]));
-      m_new[qb] = fmaxf(m_run[qb], max_halves(mx));
-    }
-  };
-  // lazy rescale (after the PV that used the old reference max)
-  auto rescale = [&](const float* m_new) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      if (__any(m_new[qb] > m_run[qb] + lazy)) {
-        const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2((m_run[qb] - m_new[qb]) * c);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) o[qb][db] *= alpha;
-        m_run[qb] = m_new[qb];
-      }
-      msc[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
-    }
-  };
-  // P^T of a half (bf16) from its S^T; row sums over the rounded values
-  auto exp_step = [&](const floatx16* sa, bf16x8 (*p)[2], float* rs, int e0, int n) {
-#pragma unroll
-    for (int e = e0; e < e0 + n; ++e) {
-      const int qb = e / 16, i = e % 16;
-      p[qb][i / 8][i % 8] = static_cast<__bf16>(fast_exp2(__builtin_fmaf(sa[qb][i], c, -msc[qb])));
-      if (i % 2 == 1) {
-        const bf16x2 pr = {p[qb][i / 8][i % 8 - 1], p[qb][i / 8][i % 8]};
-        rs[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs[qb], false);
-      }
-    }
-  };
-  // Phase A: S^T of the next half (stage stn, half nj) runs on the MFMA pipe
-  // interleaved step by step with the exponentials of the current half
-  // (sa -> p).  sched_barrier keeps
-  // the source order, pin() keeps the exponentials in this block.
-  auto phase_a = [&](const char* stn, int nj, const floatx16* sa, floatx16* sb, bf16x8 (*p)[2]) {
-    constexpr int EPS = 2 * 16 / T::KS;  // exponentials per step
-    qk8 kf[T::KS];
-#pragma unroll
-    for (int kk = 0; kk < T::KS; ++kk) kf[kk] = *reinterpret_cast<const qk8*>(stn + koff[kk] + nj * 32 * T::KROW);
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) sb[qb] = floatx16{};
-    float rs[kQB] = {0.f, 0.f};
-#pragma unroll
-    for (int step = 0; step < T::KS; ++step) {
-      exp_step(sa, p, rs, step * EPS, EPS);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) sb[qb] = mfma_32x32x16(kf[step], qf[qb][step], sb[qb]);
+  floatx16 s[2];      // S^T of a tile: keys 32j .. 32j+31 (in kperm order) x this wave's 32 queries
+  bf16x8 p[2][2];     // P^T of a tile: [half j][16-key group gg]
 
-      if ((step + 1) * EPS % 8 == 0) pin(p[((step + 1) * EPS - 1) / 16][(((step + 1) * EPS - 1) % 16) / 8]);
-      __builtin_amdgcn_sched_barrier(0);
+  // Fragment reads run kLookahead MFMAs ahead of their use (bounds the
+  // registers they hold while covering the LDS latency).
+  constexpr int kLookahead = 3;
+  auto interleave = [](int n_mfma) {
+    __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);  // LDS reads
+    for (int i = 0; i < n_mfma - kLookahead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      pin(rs[qb]);
-      l_run[qb] += rs[qb];
-    }
+    for (int i = 0; i < kLookahead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
-  // Phase B: O^T += V^T P^T of the current half on the MFMA pipe,
-  // interleaved with the row max of the next half (sb -> m_new).
-  auto phase_b = [&](const char* st, int j, bf16x8 (*p)[2], const floatx16* sb, float* m_new) {
-    constexpr int STEPS = 2 * T::DB;
-    constexpr int MPS = 2 * 16 / STEPS;  // max operations per step
-    bf16x8 va[STEPS];
+  // S^T = K Q^T of the tile in stage st
+  auto qk = [&](const char* st) {
 #pragma unroll
-    for (int k = 0; k < STEPS; ++k)
-      va[k] = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + k / T::DB] + (k % T::DB) * 32 * T::VROW);
-    float mx[kQB] = {-INFINITY, -INFINITY};
+    for (int j = 0; j < 2; ++j) {
+      s[j] = floatx16{};
 #pragma unroll
-    for (int step = 0; step < STEPS; ++step) {
-#pragma unroll
-      for (int e = step * MPS; e < (step + 1) * MPS; ++e) mx[e / 16] = fmaxf(mx[e / 16], sb[e / 16][e % 16]);
-      const int gg = step / T::DB, db = step % T::DB;
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step], p[qb][gg], o[qb][db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) m_new[qb] = fmaxf(m_run[qb], max_halves(mx[qb]));
-  };
-  // the last half: exponentials, then P V
-  auto finish_half = [&](const char* st, int j, const floatx16* sa) {
-    bf16x8 p[kQB][2];
-    float rs[kQB] = {0.f, 0.f};
-    exp_step(sa, p, rs, 0, 2 * 16);
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += rs[qb];
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[qb][gg], o[qb][db], 0, 0, 0);
+      for (int kk = 0; kk < KS; ++kk) {
+        const qk8 kf = *reinterpret_cast<const qk8*>(st + koff[kk] + j * 32 * T::KROW);
+        s[j] = mfma_32x32x16(kf, qf[kk], s[j]);
       }
+    }
+    interleave(2 * KS);
+  };
+  // O^T += V^T P^T of the tile in stage st
+  auto pv = [&](const char* st) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[j][gg], o[db], 0, 0, 0);
+        }
+    interleave(4 * DB);
+  };
+  // element i of s[j] in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4)
+  auto mask = [&](int t) {
+    const int r0 = t * kKeyTile;
+    const uint64_t mine = vis.mine;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = r0 + 32 * j + kperm(8 * (i / 4) + 4 * hl + (i & 3));
+        s[j][i] = key_visible(g, mine, key) ? s[j][i] : -INFINITY;
+      }
+  };
+  // softmax of s into p: reference max (lazy rescale of O^T and l), then
+  // exponentials rounded to bf16 and their row sum
+  auto softmax = [&]() {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[j][i], s[j][i + 1]));
+    const float m_new = fmaxf(m_run, max_halves(mx));
+    if (__any(m_new > m_run + lazy)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float msc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const __bf16 e0 = static_cast<__bf16>(fast_exp2(__builtin_fmaf(s[j][i], c, -msc)));
+        const __bf16 e1 = static_cast<__bf16>(fast_exp2(__builtin_fmaf(s[j][i + 1], c, -msc)));
+        p[j][i / 8][i % 8] = e0;
+        p[j][i / 8][i % 8 + 1] = e1;
+        const bf16x2 pr = {e0, e1};
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+      }
+    l_run += rs;
   };
 
-  // Pass 1 -- the fully visible tiles (all of them in steady state), through
-  // a software pipeline over half tiles, two halves per loop trip: S^T of the
-  // next half is computed while the current half is finished.  Tile i of the
-  // pass lives in LDS stage i % 3; tiles are prefetched two ahead.  Online
-  // softmax does not depend on key order, so the partially visible tiles
-  // are taken afterwards (pass 2) and this loop carries no masking code.
+  // Pass 1 -- the fully visible tiles (all of them in steady state).  With
+  // tile i in LDS stage i % 4, each trip of the loop first publishes tile i
+  // (everyone's loads of it have landed) and starts the load of tile i + 2
+  // into the stage of tile i - 2, which every wave finished in the previous
+  // trip.  Online softmax does not depend on key order, so the partially
+  // visible tiles are taken afterwards (pass 2) and this loop carries no
+  // masking code.
   TileWalk walk;
   walk.init(g, t_begin, t_end);
+  // every tile of the split fully visible (the steady state): no walk needed
+  bool dense = false;
+  if (t_begin < t_end && int64_t(t_end) * kKeyTile <= g.rows && g.slot_rows == g.P) {
+    const int s_lo = int((int64_t(t_begin) * kKeyTile) / g.slot_rows);
+    const int s_hi = int((int64_t(t_end) * kKeyTile - 1) / g.slot_rows);
+    const uint64_t hi = s_hi >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (s_hi + 1)) - 1);
+    dense = ((hi & ~((uint64_t(1) << s_lo) - 1)) & ~vis.all) == 0;
+  }
+  int dense_t = t_begin - 1;
   auto next_full = [&](bool first) {
+    if (dense) {
+      dense_t = first ? t_begin : dense_t + 1;
+      return dense_t < t_end ? dense_t : t_end;
+    }
     bool full = false;
     int t = walk.next(g, vis, first, &full);
     while (t < t_end && !full) t = walk.next(g, vis, false, &full);
     return t;
   };
-  int t = next_full(true);
-  if (t < t_end) {
-    issue_tile(t, 0);
-    wait_dma_all();
-    __syncthreads();
-    int tn = next_full(false);
-    if (tn < t_end) issue_tile(tn, 1);
-    int ti = 0;
-    floatx16 sa[kQB], sb[kQB];
-    float m_new[kQB];
-    bf16x8 p[kQB][2];
-    qk_half(smem, 0, sa);
-    max_half(sa, m_new);
-    rescale(m_new);
-    while (true) {
-      const char* st = smem + (ti % kStages) * T::STAGE;
-      // half 0 of tile t (sa); the next half is half 1 of the same tile
-      phase_a(st, 1, sa, sb, p);
-      phase_b(st, 0, p, sb, m_new);
-      rescale(m_new);
-      // half 1 of tile t (sb); the next half opens tile tn
-      if (tn >= t_end) {
-        finish_half(st, 1, sb);
-        break;
+  {
+    // Slots between barriers: the lead waves (0-3) run, for tile i, the MFMA
+    // phase M(i) (P V of tile i-1, S^T of tile i) in one slot and the softmax
+    // V(i) in the next; the other waves (4-7) pass one extra barrier first,
+    // so each runs M(i) while its SIMD partner runs V(i-1), and V(i) while
+    // the partner runs M(i+1).  Only the lead waves move tiles: tile i+2 is
+    // loaded (into the stage of tile i-2, last read in the slot before) as
+    // M(i) starts, and tile i+1 is waited for before the barrier that ends
+    // V(i), which publishes it.  Every wave passes the same number of
+    // barriers.
+    int tq0 = next_full(true);                        // tile i
+    int tq1 = tq0 < t_end ? next_full(false) : t_end;  // tile i + 1
+    if (tq0 < t_end) {
+      if (lead) {
+        issue_tile(tq0, 0);
+        if (tq1 < t_end) {
+          issue_tile(tq1, 1);
+          wait_vm<T::DMA>();
+        } else {
+          wait_vm<0>();
+        }
       }
-      wait_dma_all();  // tile tn has landed (for this wave) ...
-      __syncthreads();  // ... and for every wave; tile ti-1's stage is free
-      const int tnn = next_full(false);
-      if (tnn < t_end) issue_tile(tnn, (ti + 2) % kStages);
-      const char* stn = smem + ((ti + 1) % kStages) * T::STAGE;
-      phase_a(stn, 0, sb, sa, p);
-      phase_b(st, 1, p, sa, m_new);
-      rescale(m_new);
-      t = tn;
-      tn = tnn;
-      ++ti;
+      __syncthreads();
+      if (!lead) __syncthreads();
+      bool have_prev = false;  // tile i - 1 exists (its P V is pending)
+      int si = 0;              // stage of tile i
+      while (true) {
+        const bool cur = tq0 < t_end;
+        int tq2 = t_end;
+        if (tq1 < t_end) {
+          tq2 = next_full(false);
+          if (lead && tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
+        }
+        // M(i)
+        if (have_prev) pv(smem + ((si + kStages - 1) % kStages) * T::STAGE);
+        if (cur) qk(smem + si * T::STAGE);
+        __syncthreads();
+        // V(i)
+        if (cur) softmax();
+        if (lead && tq1 < t_end) {
+          if (tq2 < t_end)
+            wait_vm<T::DMA>();
+          else
+            wait_vm<0>();
+        }
+        __syncthreads();
+        if (!cur) break;
+        have_prev = true;
+        tq0 = tq1;
+        tq1 = tq2;
+        si = (si + 1) % kStages;
+      }
+      if (lead) __syncthreads();
     }
   }
 
   // Pass 2 -- partially visible tiles (warm-up, slot padding, the row tail),
   // one at a time with per-key masks.
-  {
+  if (!dense) {
     TileWalk pw;
     pw.init(g, t_begin, t_end);
     bool first = true;
@@ -543,60 +520,52 @@ __global__ __launch_bounds__(256, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       while (tp < t_end && full) tp = pw.next(g, vis, false, &full);
       if (tp >= t_end) break;
       __syncthreads();  // every wave is done with stage 0
-      issue_tile(tp, 0);
-      wait_dma_all();
-      __syncthreads();
-#pragma unroll 1
-      for (int j = 0; j < 2; ++j) {
-        floatx16 s2[kQB];
-        float m2[kQB];
-        qk_half(smem, j, s2);
-        mask_half(tp, j, s2);
-        max_half(s2, m2);
-        rescale(m2);
-        finish_half(smem, j, s2);
+      if (lead) {
+        issue_tile(tp, 0);
+        wait_vm<0>();
       }
+      __syncthreads();
+      qk(smem);
+      mask(tp);
+      softmax();
+      pv(smem);
     }
   }
 
+  const float l_tot = sum_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (!qvalid) return;
+  if (a.splits == 1) {
+    __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(b) * a.Nq + qrow) * g.H + head) * D;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float l_tot = sum_halves(l_run[qb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (m_run[qb] * c + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if (!qvalid[qb]) continue;
-    if (a.splits == 1) {
-      __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(b) * a.Nq + qrow[qb]) * g.H + head) * D;
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * db + 8 * q4 + 4 * hl;
-          const __bf16 v0 = static_cast<__bf16>(o[qb][db][4 * q4 + 0] * inv);
-          const __bf16 v1 = static_cast<__bf16>(o[qb][db][4 * q4 + 1] * inv);
-          const __bf16 v2 = static_cast<__bf16>(o[qb][db][4 * q4 + 2] * inv);
-          const __bf16 v3 = static_cast<__bf16>(o[qb][db][4 * q4 + 3] * inv);
-          uint2 w;
-          w.x = uint32_t(__builtin_bit_cast(uint16_t, v0)) | (uint32_t(__builtin_bit_cast(uint16_t, v1)) << 16);
-          w.y = uint32_t(__builtin_bit_cast(uint16_t, v2)) | (uint32_t(__builtin_bit_cast(uint16_t, v3)) << 16);
-          *reinterpret_cast<uint2*>(op + d0) = w;
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hl;
+        const __bf16 v0 = static_cast<__bf16>(o[db][4 * q4 + 0] * inv);
+        const __bf16 v1 = static_cast<__bf16>(o[db][4 * q4 + 1] * inv);
+        const __bf16 v2 = static_cast<__bf16>(o[db][4 * q4 + 2] * inv);
+        const __bf16 v3 = static_cast<__bf16>(o[db][4 * q4 + 3] * inv);
+        uint2 w;
+        w.x = uint32_t(__builtin_bit_cast(uint16_t, v0)) | (uint32_t(__builtin_bit_cast(uint16_t, v1)) << 16);
+        w.y = uint32_t(__builtin_bit_cast(uint16_t, v2)) | (uint32_t(__builtin_bit_cast(uint16_t, v3)) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = w;
       }
-      if (a.lse && hl == 0) a.lse[(int64_t(b) * g.H + head) * a.Nq + qrow[qb]] = lse_v;
-    } else {
-      float* pp = a.part_o + (((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow[qb]) * D;
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * db + 8 * q4 + 4 * hl;
-          *reinterpret_cast<float4*>(pp + d0) =
-              make_float4(o[qb][db][4 * q4] * inv, o[qb][db][4 * q4 + 1] * inv, o[qb][db][4 * q4 + 2] * inv,
-                          o[qb][db][4 * q4 + 3] * inv);
-        }
-      }
-      if (hl == 0) a.part_lse[((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow[qb]] = lse_v;
     }
+    if (a.lse && hl == 0) a.lse[(int64_t(b) * g.H + head) * a.Nq + qrow] = lse_v;
+  } else {
+    float* pp = a.part_o + (((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hl;
+        *reinterpret_cast<float4*>(pp + d0) = make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv,
+                                                          o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+      }
+    }
+    if (hl == 0) a.part_lse[((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow] = lse_v;
   }
 }
 
@@ -846,14 +815,14 @@ hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s) {
     const bool f16 = a.g.qk_dtype == SCV_FP16;
     if (a.g.D == 128) {
       if (f16)
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, _Float16>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, _Float16>), grid, dim3(512), 0, s, a);
       else
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, __bf16>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, __bf16>), grid, dim3(512), 0, s, a);
     } else {
       if (f16)
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, _Float16>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, _Float16>), grid, dim3(512), 0, s, a);
       else
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, __bf16>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, __bf16>), grid, dim3(512), 0, s, a);
     }
   } else {
     if (a.g.D == 128)
