@@ -321,6 +321,10 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       qf[kk] = __builtin_bit_cast(qk8, u);
     }
   }
+  // Q has landed before any tile load is issued: a wait the compiler sees
+  // (s_waitcnt vmcnt(0)), so that it does not place one at the first use of
+  // Q inside the tile loop, where it would also wait for the prefetched tiles.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // loop-invariant LDS byte offsets of this lane's K and V^T fragments
   int koff[KS];
