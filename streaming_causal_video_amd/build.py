@@ -53,13 +53,8 @@ COMMON = [
 ]
 
 
-# Per-source additions.  The attention kernels never produce or consume NaN
-# (masked scores are -inf and every -inf - -inf is guarded), so they run with
-# the IEEE mode bit off: v_max_f32 then needs no quieting of its inputs,
-# which would otherwise double the cost of the row max.
-PER_FILE = {
-    "chunk_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-}
+# Per-source additions (none at present).
+PER_FILE: dict = {}
 
 
 def _compile(src: str, hipcc: str) -> str:

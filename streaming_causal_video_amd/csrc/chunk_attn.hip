@@ -145,8 +145,8 @@ __device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int 
 // per lane).  Both tiles carry an XOR swizzle of 16-byte chunks that puts
 // any 16 consecutive lanes of a fragment read on distinct banks (64 banks
 // of 4 bytes).
-// Softmax rescaling is lazy: the reference max moves only when a row's
-// max grows by more than 2^8 (so exponentials stay <= 256).
+// Softmax rescaling is lazy: the reference max moves only when an
+// exponential would exceed 2^10, detected from the row sums after the fact.
 // ---------------------------------------------------------------------------
 // Direct global -> LDS load of 16 bytes per lane: lane l writes LDS byte
 // address lds_base + 16*l (lds_base wave-uniform, via M0) from base + voff
@@ -173,6 +173,15 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max(a, b, c) as one v_max3_f32.  Through fmaxf the compiler would first
+// quiet the NaNs of each input (one more instruction per element); the
+// inputs here are MFMA results and running maxima, never NaN.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // LDS row r of a K tile holds key row kperm(r) of the tile.
@@ -338,8 +347,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = floatx16{};
   float m_run = -INFINITY, l_run = 0.f;
+  float msc_run = 0.f;                 // m_run * c (0 while m_run is -inf)
   const float c = a.scale_log2;
-  const float lazy = 8.f / c;  // raw-score growth that forces a rescale (2^8)
+  constexpr float kPBound = 1024.f;    // largest exponential kept (2^10)
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 
   // Fragment reads run kLookahead MFMAs ahead of their use (bounds the
   // registers they hold while covering the LDS latency).
-  constexpr int kLookahead = 3;
+  constexpr int kLookahead = 8;
   auto interleave = [](int n_mfma) {
     __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);  // LDS reads
     for (int i = 0; i < n_mfma - kLookahead; ++i) {
@@ -357,21 +367,21 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     }
     for (int i = 0; i < kLookahead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
-  // S^T = K Q^T of the tile in stage st
-  auto qk = [&](const char* st) {
+  // S^T = K Q^T of the tile in stage st (the two 32-key halves alternate, so
+  // no MFMA waits on the one just issued)
+  auto qk_ops = [&](const char* st) {
+    s[0] = floatx16{};
+    s[1] = floatx16{};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      s[j] = floatx16{};
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+      for (int j = 0; j < 2; ++j) {
         const qk8 kf = *reinterpret_cast<const qk8*>(st + koff[kk] + j * 32 * T::KROW);
         s[j] = mfma_32x32x16(kf, qf[kk], s[j]);
       }
-    }
-    interleave(2 * KS);
   };
   // O^T += V^T P^T of the tile in stage st
-  auto pv = [&](const char* st) {
+  auto pv_ops = [&](const char* st) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -381,7 +391,21 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
           const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[j][gg], o[db], 0, 0, 0);
         }
+  };
+  auto qk = [&](const char* st) {
+    qk_ops(st);
+    interleave(2 * KS);
+  };
+  auto pv = [&](const char* st) {
+    pv_ops(st);
     interleave(4 * DB);
+  };
+  // the MFMA phase of a steady-state trip: P V of the previous tile and S^T
+  // of this one as one stream, so the fragment reads stay ahead across both
+  auto pv_qk = [&](const char* stp, const char* st) {
+    pv_ops(stp);
+    qk_ops(st);
+    interleave(4 * DB + 2 * KS);
   };
   // element i of s[j] in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4)
   auto mask = [&](int t) {
@@ -395,36 +419,55 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         s[j][i] = key_visible(g, mine, key) ? s[j][i] : -INFINITY;
       }
   };
-  // softmax of s into p: reference max (lazy rescale of O^T and l), then
-  // exponentials rounded to bf16 and their row sum
-  auto softmax = [&]() {
-    float mx = -INFINITY;
+  // Exponentials of s against the reference offset msc, rounded to bf16 into
+  // p, with their sums over this lane's 32 keys (two chains).
+  auto exps = [&](float msc, float* rs) {
+    rs[0] = rs[1] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 16; i += 2)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[j][i], s[j][i + 1]));
-    const float m_new = fmaxf(m_run, max_halves(mx));
-    if (__any(m_new > m_run + lazy)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m_run = m_new;
-    }
-    const float msc = (m_run == -INFINITY) ? 0.f : m_run * c;
-    float rs = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
+      for (int j = 0; j < 2; ++j) {
         const __bf16 e0 = static_cast<__bf16>(fast_exp2(__builtin_fmaf(s[j][i], c, -msc)));
         const __bf16 e1 = static_cast<__bf16>(fast_exp2(__builtin_fmaf(s[j][i + 1], c, -msc)));
         p[j][i / 8][i % 8] = e0;
         p[j][i / 8][i % 8 + 1] = e1;
         const bf16x2 pr = {e0, e1};
-        rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+        rs[j] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs[j], false);
       }
-    l_run += rs;
+  };
+  // Softmax of s into p.  The exponentials are taken against the running
+  // reference first; their row sums (needed anyway) show whether an element
+  // exceeds 2^10 or no reference exists yet.  Only then is the row max
+  // computed, the reference raised, O^T and l rescaled and the exponentials
+  // redone -- so elements never exceed 2^10 and the common path has no
+  // max reduction in front of the exponentials.
+  auto softmax = [&]() {
+    float rs[2];
+    exps(msc_run, rs);
+    if (__any((rs[0] + rs[1] > kPBound) || (m_run == -INFINITY))) {
+      // row max with v_max3_f32 issued directly (see vmax3); the fence makes
+      // the wait states an MFMA result needs before such reads explicit
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]));
+      auto x = [&](int e) { return s[e / 16][e % 16]; };
+      float ch[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ch[q] = vmax3(x(8 * q), x(8 * q + 1), x(8 * q + 2));
+      const float e7 = vmax3(x(7), x(23), x(31));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ch[q] = vmax3(ch[q], x(8 * q + 3), x(8 * q + 4));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ch[q] = vmax3(ch[q], x(8 * q + 5), x(8 * q + 6));
+      const float mx = vmax3(vmax3(ch[0], ch[1], e7), vmax3(ch[2], ch[3], x(15)), m_run);
+      const float m_new = max_halves(mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+      msc_run = (m_run == -INFINITY) ? 0.f : m_run * c;
+      exps(msc_run, rs);
+    }
+    l_run += rs[0] + rs[1];
   };
 
   // Pass 1 -- the fully visible tiles (all of them in steady state).  With
@@ -489,8 +532,14 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
           if (lead && tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
         }
         // M(i)
-        if (have_prev) pv(smem + ((si + kStages - 1) % kStages) * T::STAGE);
-        if (cur) qk(smem + si * T::STAGE);
+        const char* st = smem + si * T::STAGE;
+        const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
+        if (have_prev && cur) {
+          pv_qk(stp, st);
+        } else {
+          if (have_prev) pv(stp);
+          if (cur) qk(st);
+        }
         __syncthreads();
         // V(i)
         if (cur) softmax();
