@@ -358,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 
   // Fragment reads run kLookahead MFMAs ahead of their use (bounds the
   // registers they hold while covering the LDS latency).
-  constexpr int kLookahead = 8;
+  constexpr int kLookahead = 3;
   auto interleave = [](int n_mfma) {
     __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);  // LDS reads
     for (int i = 0; i < n_mfma - kLookahead; ++i) {
@@ -400,13 +400,6 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     pv_ops(st);
     interleave(4 * DB);
   };
-  // the MFMA phase of a steady-state trip: P V of the previous tile and S^T
-  // of this one as one stream, so the fragment reads stay ahead across both
-  auto pv_qk = [&](const char* stp, const char* st) {
-    pv_ops(stp);
-    qk_ops(st);
-    interleave(4 * DB + 2 * KS);
-  };
   // element i of s[j] in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4)
   auto mask = [&](int t) {
     const int r0 = t * kKeyTile;
@@ -420,20 +413,24 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       }
   };
   // Exponentials of s against the reference offset msc, rounded to bf16 into
-  // p, with their sums over this lane's 32 keys (two chains).
+  // p, with their fp32 sums over this lane's 32 keys (four chains).  The sums
+  // use plain adds: v_dot2c_f32_bf16 would stall while the SIMD's other wave
+  // streams MFMAs.
   auto exps = [&](float msc, float* rs) {
-    rs[0] = rs[1] = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 16; i += 2)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const __bf16 e0 = static_cast<__bf16>(fast_exp2(__builtin_fmaf(s[j][i], c, -msc)));
-        const __bf16 e1 = static_cast<__bf16>(fast_exp2(__builtin_fmaf(s[j][i + 1], c, -msc)));
-        p[j][i / 8][i % 8] = e0;
-        p[j][i / 8][i % 8 + 1] = e1;
-        const bf16x2 pr = {e0, e1};
-        rs[j] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs[j], false);
+        const float f0 = fast_exp2(__builtin_fmaf(s[j][i], c, -msc));
+        const float f1 = fast_exp2(__builtin_fmaf(s[j][i + 1], c, -msc));
+        p[j][i / 8][i % 8] = static_cast<__bf16>(f0);
+        p[j][i / 8][i % 8 + 1] = static_cast<__bf16>(f1);
+        acc[2 * j] += f0;
+        acc[2 * j + 1] += f1;
       }
+    rs[0] = acc[0] + acc[1];
+    rs[1] = acc[2] + acc[3];
   };
   // Softmax of s into p.  The exponentials are taken against the running
   // reference first; their row sums (needed anyway) show whether an element
@@ -534,12 +531,8 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         // M(i)
         const char* st = smem + si * T::STAGE;
         const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
-        if (have_prev && cur) {
-          pv_qk(stp, st);
-        } else {
-          if (have_prev) pv(stp);
-          if (cur) qk(st);
-        }
+        if (have_prev) pv(stp);
+        if (cur) qk(st);
         __syncthreads();
         // V(i)
         if (cur) softmax();
