@@ -191,7 +191,7 @@ constexpr int kPPWaves = 8;                  // waves per workgroup (2 per SIMD)
 constexpr int kRowsBf16 = 32 * kPPWaves;     // 256 query rows per workgroup
 static_assert(kRowsBf16 == kAttnRowsBf16, "host and kernel agree on the query tile");
 constexpr int kStages = 4;                   // LDS tile ring
-constexpr int kDmaWaves = 4;                 // waves 0-3 move the tiles
+constexpr int kDmaWaves = kPPWaves;          // every wave moves its share of a tile
 
 template <int D>
 struct Bf16Tile {
@@ -293,8 +293,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   const char* vbase = static_cast<const char*>(a.cache_v) + (int64_t(b) * g.H + head) * D * vpitch;
   // per-lane source offsets inside a tile (loop invariant); LDS is filled
   // linearly and the swizzle is applied on the source side
-  // (only waves 0 .. kDmaWaves-1 load; dw is their index)
-  const int dw = wave & (kDmaWaves - 1);
+  const int dw = wave;
   uint32_t kvo[T::K_DMA], vvo[T::V_DMA];
 #pragma unroll
   for (int i = 0; i < T::K_DMA; ++i) {
@@ -500,22 +499,20 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     // phase M(i) (P V of tile i-1, S^T of tile i) in one slot and the softmax
     // V(i) in the next; the other waves (4-7) pass one extra barrier first,
     // so each runs M(i) while its SIMD partner runs V(i-1), and V(i) while
-    // the partner runs M(i+1).  Only the lead waves move tiles: tile i+2 is
-    // loaded (into the stage of tile i-2, last read in the slot before) as
-    // M(i) starts, and tile i+1 is waited for before the barrier that ends
-    // V(i), which publishes it.  Every wave passes the same number of
-    // barriers.
+    // the partner runs M(i+1).  Every wave loads its share of each tile:
+    // tile i+2 (into the stage of tile i-2, which both groups finished before
+    // the barrier that starts the wave's trip) as its M(i) starts; tile i+1
+    // is waited for before the barrier that ends the lead waves' V(i), which
+    // publishes it.  Every wave passes the same number of barriers.
     int tq0 = next_full(true);                        // tile i
     int tq1 = tq0 < t_end ? next_full(false) : t_end;  // tile i + 1
     if (tq0 < t_end) {
-      if (lead) {
-        issue_tile(tq0, 0);
-        if (tq1 < t_end) {
-          issue_tile(tq1, 1);
-          wait_vm<T::DMA>();
-        } else {
-          wait_vm<0>();
-        }
+      issue_tile(tq0, 0);
+      if (tq1 < t_end) {
+        issue_tile(tq1, 1);
+        wait_vm<T::DMA>();
+      } else {
+        wait_vm<0>();
       }
       __syncthreads();
       if (!lead) __syncthreads();
@@ -524,24 +521,30 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       while (true) {
         const bool cur = tq0 < t_end;
         int tq2 = t_end;
+        auto wait_next = [&]() {
+          if (tq1 < t_end) {
+            if (tq2 < t_end)
+              wait_vm<T::DMA>();
+            else
+              wait_vm<0>();
+          }
+        };
         if (tq1 < t_end) {
           tq2 = next_full(false);
-          if (lead && tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
+          if (tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
         }
         // M(i)
         const char* st = smem + si * T::STAGE;
         const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
         if (have_prev) pv(stp);
         if (cur) qk(st);
+        // each wave's share of tile i+1 has landed before the barrier after
+        // which the first reader (a lead wave in M(i+1)) may start
+        if (!lead) wait_next();
         __syncthreads();
         // V(i)
         if (cur) softmax();
-        if (lead && tq1 < t_end) {
-          if (tq2 < t_end)
-            wait_vm<T::DMA>();
-          else
-            wait_vm<0>();
-        }
+        if (lead) wait_next();
         __syncthreads();
         if (!cur) break;
         have_prev = true;
@@ -566,10 +569,8 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       while (tp < t_end && full) tp = pw.next(g, vis, false, &full);
       if (tp >= t_end) break;
       __syncthreads();  // every wave is done with stage 0
-      if (lead) {
-        issue_tile(tp, 0);
-        wait_vm<0>();
-      }
+      issue_tile(tp, 0);
+      wait_vm<0>();
       __syncthreads();
       qk(smem);
       mask(tp);
