@@ -184,6 +184,24 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return r;
 }
 
+// Workgroups are handed to the 8 XCDs of the chip round robin by linear
+// index, each XCD with its own L2.  Renumber them so that every XCD runs a
+// contiguous range of (query tile fastest, then head, then stream/split):
+// the query tiles of one head then share that head's K/V in one L2 instead
+// of each XCD fetching it from HBM.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_remap(int* x, int* y, int* z) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int n = nx * ny * gridDim.z;
+  const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int xcd = id % kXcds, k = id / kXcds;
+  const int base = n / kXcds, extra = n % kXcds;  // XCDs below `extra` run one more
+  const int logical = xcd * base + min(xcd, extra) + k;
+  *x = logical % nx;
+  *y = (logical / nx) % ny;
+  *z = logical / (nx * ny);
+}
+
 // LDS row r of a K tile holds key row kperm(r) of the tile.
 __device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -276,8 +294,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lead = wave < 4;  // MFMA phase first
   const int hl = lane >> 5, l32 = lane & 31;
-  const int qtile = blockIdx.x, head = blockIdx.y;
-  const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
+  int qtile, head, bz;
+  xcd_remap(&qtile, &head, &bz);
+  const int b = bz / a.splits, split = bz % a.splits;
   const int qrow = qtile * kRowsBf16 + wave * 32 + l32;
   const bool qvalid = qrow < a.Nq;
 
