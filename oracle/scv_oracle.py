@@ -41,7 +41,17 @@ Readings taken where they are silent (each also listed in the design doc):
   R = W + max_query_chunks*C frames and frame g >= S_f lives in slot
   S_f + (g mod R); R10 only frames present in the cache are visible (warm-up);
   R11 angles are fp64 products pos*omega, cos/sin are then rounded to fp32;
-  R12 a query row that sees no key returns O = 0 and lse = -inf.
+  R12 a query row that sees no key returns O = 0 and lse = -inf;
+  R17 RoPE refresh (the pages' periodic reset of the position offset): the
+  time position of frame g of stream b is g - offset[b]; refresh(delta) turns
+  the time pairs of every cached key by -delta[b]*omega_t (its time position
+  drops by delta[b]) and adds delta[b] to offset[b]; stamps, slots and
+  visibility stay on global frame indices, so attention is unchanged in exact
+  arithmetic; R18 sink update (the pages' adaptive sink): sink slot j takes
+  frame first[b] + j -- its k rotated at that frame's own time position, its
+  v, and the frame as stamp -- and the ring is not touched; R19 a key in a
+  sink slot is seen by every query chunk that ends after its frame (no
+  window rule), a key in a ring slot by R7/R8.
 
 Pinned by tests/test_oracle_*.py (brute force, closed forms, the RoPE
 relative-position invariant, torch SDPA in float64, rolling-cache == masked
@@ -64,6 +74,7 @@ __all__ = [
     "rope3d",
     "frame_slot",
     "frame_visible",
+    "slot_visible",
     "attention",
     "merge_partials",
     "OracleCache",
@@ -220,6 +231,19 @@ def frame_visible(g: int, chunk_start: int, chunk_frames: int, sink_frames: int,
     return g < sink_frames or g >= chunk_start - window_frames
 
 
+def slot_visible(slot: int, g: int, chunk_start: int, chunk_frames: int, sink_frames: int, window_frames: int) -> bool:
+    """Visibility of the key held in cache slot ``slot`` (stamped with frame g)
+    by slot class (reading R19): sink slots are the global anchor, seen by
+    every query chunk that ends after their frame; ring slots follow
+    frame_visible.  With the initial frames in the sink (R6) this is exactly
+    frame_visible of the slot's frame."""
+    if g < 0:
+        return False
+    if slot < sink_frames:
+        return g < chunk_start + chunk_frames
+    return frame_visible(g, chunk_start, chunk_frames, sink_frames, window_frames)
+
+
 # --------------------------------------------------------------------------
 # a4 / a5 -- attention and the split/merge identity
 # --------------------------------------------------------------------------
@@ -275,6 +299,8 @@ class OracleCache:
         rotated here at their global times; [SDV2-blog] 2 sink tokens)."""
         s = self.spec
         self.stamps = np.full((s.batch, s.n_slots), -1, dtype=np.int64)
+        # time position of frame g of stream b is g - pos_offset[b] (R17)
+        self.pos_offset = np.zeros(s.batch, dtype=np.int64)
         self.k: List[Dict[int, np.ndarray]] = [dict() for _ in range(s.batch)]
         self.v: List[Dict[int, np.ndarray]] = [dict() for _ in range(s.batch)]
         if sink_k is not None:
@@ -283,11 +309,12 @@ class OracleCache:
 
     # rope3d_apply(x, t0, grid) ----------------------------------------------
     def rope3d_apply(self, x: np.ndarray, t0: Sequence[int], n_frames: int) -> np.ndarray:
-        """Rotate x [B, n_frames*P, H, d]; stream b's frames start at t0[b]."""
+        """Rotate x [B, n_frames*P, H, d]; stream b's frames start at global
+        frame t0[b], whose time position is t0[b] - pos_offset[b] (R17)."""
         s = self.spec
         out = np.empty(x.shape, dtype=np.float64)
         for b in range(s.batch):
-            t, h, w = token_positions(t0[b], n_frames, s.grid_h, s.grid_w)
+            t, h, w = token_positions(int(t0[b]) - int(self.pos_offset[b]), n_frames, s.grid_h, s.grid_w)
             out[b] = rope3d(x[b], t, h, w, s.split, s.base)
         return out
 
@@ -310,6 +337,39 @@ class OracleCache:
         self.kv_append_roll(self.rope3d_apply(k, t0, n_frames), v, t0, n_frames)
         return self.rope3d_apply(q, t0, n_frames)
 
+    # RoPE refresh ([SDV2-blog] 2; [SDV2-summary] 2.A.2) -------------------
+    def rope_refresh(self, delta: Sequence[int]):
+        """Move stream b's time origin forward by delta[b] frames (R17): every
+        cached key -- sink and ring -- has its time pairs turned by
+        -delta[b]*omega_t, i.e. it becomes the key rotated at time position
+        (its frame - new offset); later rotations of stream b use the new
+        offset.  Values, stamps and slots are unchanged."""
+        s = self.spec
+        for b in range(s.batch):
+            dlt = int(delta[b])
+            for slot, kk in self.k[b].items():
+                n = kk.shape[0]
+                zero = np.zeros(n, dtype=np.int64)
+                self.k[b][slot] = rope3d(kk, np.full(n, -dlt, dtype=np.int64), zero, zero, s.split, s.base)
+            self.pos_offset[b] += dlt
+
+    # sink update ([SDV2-blog] 2; [SDV2-summary] 2.A.2) ----------------------
+    def sink_update(self, k: np.ndarray, v: np.ndarray, first_frame: Sequence[int], n_frames: int):
+        """Adaptive sink (R18): sink slot j (j < n_frames <= S_f) of stream b
+        takes frame first_frame[b] + j -- raw k [B, n_frames*P, H, d] rotated
+        at that frame's time position, v as given -- and is stamped with that
+        frame.  Ring slots are not touched."""
+        s = self.spec
+        if not 1 <= n_frames <= s.sink_frames:
+            raise ValueError("sink update needs 1 <= n_frames <= sink_frames")
+        P = s.tokens_per_frame
+        k_rot = self.rope3d_apply(k, first_frame, n_frames)
+        for b in range(s.batch):
+            for j in range(n_frames):
+                self.k[b][j] = np.array(k_rot[b, j * P : (j + 1) * P], dtype=np.float64)
+                self.v[b][j] = np.array(v[b, j * P : (j + 1) * P], dtype=np.float64)
+                self.stamps[b, j] = int(first_frame[b]) + j
+
     # chunk_attention(q, cache) -> o ----------------------------------------
     def visible_slots(self, b: int, chunk_start: int) -> List[int]:
         s = self.spec
@@ -317,7 +377,8 @@ class OracleCache:
             slot
             for slot in range(s.n_slots)
             if self.stamps[b, slot] >= 0
-            and frame_visible(int(self.stamps[b, slot]), chunk_start, s.chunk_frames, s.sink_frames, s.window_frames)
+            and slot_visible(slot, int(self.stamps[b, slot]), chunk_start, s.chunk_frames, s.sink_frames,
+                             s.window_frames)
         ]
 
     def chunk_attention(self, q_rot: np.ndarray, t0: Sequence[int], n_frames: int, rows: Optional[np.ndarray] = None):

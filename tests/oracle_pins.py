@@ -395,6 +395,153 @@ def check_shift_invariance_of_attention():
         assert np.max(np.abs(run(delta) - ref)) <= 1e-9, delta
 
 
+# ------------------------------------------- RoPE refresh and sink update ---
+def _explicit_rot(x, pos):
+    """Explicit block-diagonal rotation for split (2, 2, 2) (one pair per
+    axis, omega_0 = 1, so each angle is the position itself)."""
+    d = x.shape[-1]
+    R = np.zeros((d, d))
+    for blk, p in enumerate(pos):
+        c, s = math.cos(float(p)), math.sin(float(p))
+        R[2 * blk : 2 * blk + 2, 2 * blk : 2 * blk + 2] = [[c, -s], [s, c]]
+    return R @ x
+
+
+def check_refresh_keeps_attention():
+    """A RoPE refresh changes no output: two caches fed the same streams, one
+    of them refreshed twice along the way, give the same O and lse on every
+    chunk (scores depend only on differences of time positions, and the
+    refresh moves keys and later queries by the same amount)."""
+    rng = np.random.default_rng(61)
+    spec = O.CacheSpec(batch=2, heads=2, head_dim=12, split=(4, 4, 4), base=10000.0, grid_h=2, grid_w=3,
+                       sink_frames=1, window_frames=4, chunk_frames=2)
+    P, H, d, C = 6, 2, 12, 2
+    plain, fresh = O.OracleCache(spec), O.OracleCache(spec)
+    sk, sv = rng.standard_normal((2, P, H, d)), rng.standard_normal((2, P, H, d))
+    plain.init(sk, sv)
+    fresh.init(sk, sv)
+    refresh_at = {3: [5, 1000], 6: [1, 5]}
+    for step in range(9):
+        t0 = [1 + C * step, 1000 + C * step]
+        q, k, v = (rng.standard_normal((2, C * P, H, d)) for _ in range(3))
+        if step in refresh_at:
+            fresh.rope_refresh(refresh_at[step])
+        qa = plain.rope3d_append(q, k, v, t0, C)
+        qb = fresh.rope3d_append(q, k, v, t0, C)
+        oa, la = plain.chunk_attention(qa, t0, C)
+        ob, lb = fresh.chunk_attention(qb, t0, C)
+        assert np.max(np.abs(oa - ob)) <= 1e-9, step
+        assert np.max(np.abs(la - lb)) <= 1e-9, step
+        assert np.array_equal(plain.stamps, fresh.stamps)
+    assert list(fresh.pos_offset) == [6, 1005]
+
+
+def check_refresh_equals_rotation_at_earlier_time():
+    """After refresh(delta) every cached key equals its raw key rotated by
+    explicit rotation matrices at time position (frame - delta), sink
+    included, and the next append rotates at (frame - delta) as well."""
+    rng = np.random.default_rng(62)
+    spec = O.CacheSpec(batch=1, heads=1, head_dim=6, split=(2, 2, 2), base=10000.0, grid_h=2, grid_w=2,
+                       sink_frames=1, window_frames=2, chunk_frames=1)
+    cache = O.OracleCache(spec)
+    raw = {}
+    for g in range(5):
+        q, k, v = (rng.standard_normal((1, 4, 1, 6)) for _ in range(3))
+        raw[g] = k
+        cache.rope3d_append(q, k, v, [g], 1)
+    cache.rope_refresh([3])
+    for slot in range(spec.n_slots):
+        g = int(cache.stamps[0, slot])
+        for p in range(4):
+            want = _explicit_rot(raw[g][0, p, 0], (g - 3, p // 2, p % 2))
+            assert np.max(np.abs(cache.k[0][slot][p, 0] - want)) <= 1e-12, (slot, g, p)
+    x = rng.standard_normal((1, 4, 1, 6))
+    y = cache.rope3d_apply(x, [5], 1)
+    for p in range(4):
+        assert np.max(np.abs(y[0, p, 0] - _explicit_rot(x[0, p, 0], (2, p // 2, p % 2)))) <= 1e-12
+
+
+def _sink_brute(n_calls, chunks_per_call, update_call, update_frame_in_call, seed):
+    """Stream of single-frame chunks (C = 1, S_f = 1, W = 2, d = 6), each call
+    appending ``chunks_per_call`` frames; in call ``update_call`` the sink
+    takes the k/v of that call's frame ``update_frame_in_call``.  Every
+    chunk's output equals brute-force attention over an explicit key list --
+    the sink entry (seen by a chunk iff the chunk does not end before its
+    frame, whatever the window) plus the window frames -- with keys rotated
+    by explicit matrices at their own frames; the update leaves the ring
+    untouched."""
+    rng = np.random.default_rng(seed)
+    d, P, W, Sf, n = 6, 4, 2, 1, chunks_per_call
+    spec = O.CacheSpec(batch=1, heads=1, head_dim=d, split=(2, 2, 2), base=10000.0, grid_h=2, grid_w=2,
+                       sink_frames=Sf, window_frames=W, chunk_frames=1, max_query_chunks=n)
+    cache = O.OracleCache(spec)
+    hist = {}  # frame -> (rotated keys, values)
+    sink = None  # (frame, keys, values)
+    for call in range(n_calls):
+        t0 = call * n
+        q, k, v = (rng.standard_normal((1, n * P, 1, d)) for _ in range(3))
+        q_rot = cache.rope3d_append(q, k, v, [t0], n)
+        for f in range(n):
+            g = t0 + f
+            hist[g] = ([_explicit_rot(k[0, f * P + p, 0], (g, p // 2, p % 2)) for p in range(P)],
+                       [v[0, f * P + p, 0] for p in range(P)])
+        if call == 0:
+            sink = (0, *hist[0])
+        if call == update_call:
+            ring_k = {s_: cache.k[0][s_].copy() for s_ in range(Sf, spec.n_slots) if s_ in cache.k[0]}
+            ring_stamps = cache.stamps[0, Sf:].copy()
+            u = update_frame_in_call
+            cache.sink_update(k[:, u * P : (u + 1) * P], v[:, u * P : (u + 1) * P], [t0 + u], 1)
+            sink = (t0 + u, *hist[t0 + u])
+            assert np.array_equal(cache.stamps[0, Sf:], ring_stamps)
+            for s_, kk in ring_k.items():
+                assert np.array_equal(cache.k[0][s_], kk)
+            assert cache.stamps[0, 0] == t0 + u
+        o, _ = cache.chunk_attention(q_rot, [t0], n)
+        for f in range(n):
+            g = t0 + f
+            entries = []
+            if sink[0] <= g:
+                entries += list(zip(sink[1], sink[2]))
+            for fr in range(max(Sf, g - W), g + 1):
+                entries += list(zip(*hist[fr]))
+            for p in range(P):
+                qr = _explicit_rot(q[0, f * P + p, 0], (g, p // 2, p % 2))
+                scores = [sum(qr[c] * kk[c] for c in range(d)) / math.sqrt(d) for kk, _ in entries]
+                m = max(scores)
+                e = [math.exp(x - m) for x in scores]
+                tot = sum(e)
+                ob = sum((e[j] / tot) * entries[j][1] for j in range(len(e)))
+                assert np.max(np.abs(o[0, f * P + p, 0] - ob)) <= 1e-12, (call, f, p)
+
+
+def check_sink_update_brute_force():
+    # one chunk per call; the sink takes the newest frame at frame 5
+    _sink_brute(12, 1, 5, 0, 63)
+    # two chunks per call; the sink takes the second chunk's frame, which the
+    # first chunk of the same call must not see
+    _sink_brute(7, 2, 3, 1, 65)
+
+
+def check_sink_update_with_the_sink_itself_is_a_no_op():
+    """Replacing the sink by the initial frame's own k/v changes nothing."""
+    rng = np.random.default_rng(64)
+    spec = O.CacheSpec(batch=1, heads=2, head_dim=12, split=(4, 4, 4), base=10000.0, grid_h=2, grid_w=2,
+                       sink_frames=1, window_frames=3, chunk_frames=2)
+    a, b = O.OracleCache(spec), O.OracleCache(spec)
+    sk, sv = rng.standard_normal((1, 4, 2, 12)), rng.standard_normal((1, 4, 2, 12))
+    a.init(sk, sv)
+    b.init(sk, sv)
+    b.sink_update(sk, sv, [0], 1)
+    for step in range(4):
+        t0 = [1 + 2 * step]
+        q, k, v = (rng.standard_normal((1, 8, 2, 12)) for _ in range(3))
+        oa, la = a.chunk_attention(a.rope3d_append(q, k, v, t0, 2), t0, 2)
+        ob, lb = b.chunk_attention(b.rope3d_append(q, k, v, t0, 2), t0, 2)
+        assert np.max(np.abs(oa - ob)) <= 1e-15 and np.max(np.abs(la - lb)) <= 1e-15
+        assert np.array_equal(a.stamps, b.stamps)
+
+
 ALL_CHECKS = [
     check_golden_unit_vectors,
     check_frequency_ladder,
@@ -413,4 +560,8 @@ ALL_CHECKS = [
     check_rolling_cache_equals_masked_full_attention,
     check_stream_brute_force,
     check_shift_invariance_of_attention,
+    check_refresh_keeps_attention,
+    check_refresh_equals_rotation_at_earlier_time,
+    check_sink_update_brute_force,
+    check_sink_update_with_the_sink_itself_is_a_no_op,
 ]

@@ -81,6 +81,36 @@ def _frequencies_variant(kind):
     return rope_frequencies
 
 
+def _refresh_variant(kind):
+    def rope_refresh(self, delta):
+        s = self.spec
+        for b in range(s.batch):
+            dlt = int(delta[b])
+            for slot, kk in self.k[b].items():
+                if kind == "skips_sink" and slot < s.sink_frames:
+                    continue
+                n = kk.shape[0]
+                t = np.full(n, dlt if kind == "wrong_sign" else -dlt, dtype=np.int64)
+                hw = t if kind == "turns_all_axes" else np.zeros(n, dtype=np.int64)
+                self.k[b][slot] = O.rope3d(kk, t, hw, hw, s.split, s.base)
+            if kind != "forgets_offset":
+                self.pos_offset[b] += dlt
+
+    return rope_refresh
+
+
+def _sink_update_at_slot_time(self, k, v, first_frame, n_frames):
+    # rotates the new sink at the time of the slot it replaces, not its frame
+    s = self.spec
+    P = s.tokens_per_frame
+    k_rot = self.rope3d_apply(k, [0] * s.batch, n_frames)
+    for b in range(s.batch):
+        for j in range(n_frames):
+            self.k[b][j] = k_rot[b, j * P : (j + 1) * P]
+            self.v[b][j] = np.asarray(v[b, j * P : (j + 1) * P], dtype=np.float64)
+            self.stamps[b, j] = int(first_frame[b]) + j
+
+
 MUTATIONS = {
     "rope_sin_sign": ("rope3d", _rope3d_variant(sign=-1.0)),
     "rope_half_split_pairs": ("rope3d", _rope3d_variant(half_split=True)),
@@ -101,6 +131,14 @@ MUTATIONS = {
     "attention_transposed_v": ("attention", _attention_variant("transposed_v")),
     "attention_lse_dropped_max": ("attention", _attention_variant("lse_no_max")),
     "attention_drops_a_key": ("attention", _attention_variant("drop_last_key")),
+    "refresh_wrong_sign": ("OracleCache.rope_refresh", _refresh_variant("wrong_sign")),
+    "refresh_forgets_offset": ("OracleCache.rope_refresh", _refresh_variant("forgets_offset")),
+    "refresh_skips_sink": ("OracleCache.rope_refresh", _refresh_variant("skips_sink")),
+    "refresh_turns_all_axes": ("OracleCache.rope_refresh", _refresh_variant("turns_all_axes")),
+    "sink_update_at_slot_time": ("OracleCache.sink_update", _sink_update_at_slot_time),
+    "sink_follows_window": ("slot_visible", lambda slot, g, s, C, sf, W: O.frame_visible(g, s, C, sf, W)),
+    "sink_not_causal": ("slot_visible", lambda slot, g, s, C, sf, W: g >= 0 if slot < sf else
+                        O.frame_visible(g, s, C, sf, W)),
     "merge_unweighted": (
         "merge_partials",
         lambda o, l: (np.asarray(o).mean(axis=0), np.logaddexp.reduce(np.asarray(l), axis=0)),
@@ -111,7 +149,11 @@ MUTATIONS = {
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
-    monkeypatch.setattr(O, attr, fn)
+    owner = O
+    if "." in attr:
+        cls, attr = attr.split(".")
+        owner = getattr(O, cls)
+    monkeypatch.setattr(owner, attr, fn)
     caught = []
     for check in pins.ALL_CHECKS:
         try:
