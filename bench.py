@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md
-    "wan1.3b-480p": {"source": "be23ad98156aa594", "kv_splits": 1, "bytes_per_launch": 272059455},
+    "wan1.3b-480p": {"source": "d838ace6bebf75d5", "kv_splits": 1, "bytes_per_launch": 272069101},
 }
 KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
 
@@ -131,6 +131,39 @@ def cpu_baseline(w, target_s=12.0):
         f"query rows (random, all {w.heads} heads, all visible keys) of {w.name}; {spent:.1f} s of CPU time; "
         f"cache filled by the oracle beforehand (untimed)",
     }
+
+
+def time_refresh_and_sink(r, w, reps=20):
+    """HIP-event times of the RoPE refresh (every cached key's time pairs,
+    one launch) and of a one-frame sink update, on the launch stream, after
+    the timed steps (they change the cache state the steps ran on)."""
+    import torch
+
+    eb = 2 if w.dtype == "bf16" else 4
+    P, H, D, B = w.tokens_per_frame, w.heads, w.head_dim, w.batch
+    cached_rows = w.n_slots * P  # every slot holds a frame in the steady state
+    refresh_bytes = 2 * B * H * cached_rows * w.split[0] * eb
+    sink_bytes = 4 * B * P * H * D * eb  # read k, v; write k_rot, v^T
+    k1 = r.k[:, :P].contiguous()
+    v1 = r.v[:, :P].contiguous()
+    first = list(w.t0)
+    res = {}
+    for name, fn, nbytes in (
+        ("rope_refresh", lambda: r.cache.rope_refresh([1] * B), refresh_bytes),
+        ("sink_update", lambda: r.cache.sink_update(k1, v1, first, 1), sink_bytes),
+    ):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": us, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    return res
 
 
 def main():
@@ -240,6 +273,7 @@ def main():
     }
     if r.splits > 1:
         out["attn_ms_includes_merge"] = True
+    out["next_rows"] = time_refresh_and_sink(r, w)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -34,10 +34,15 @@
  *    frame it holds (-1 = empty).
  *  - Query frames of stream b are t0[b] .. t0[b]+n_frames-1, grouped into
  *    chunks of chunk_frames frames from t0[b].  A query of the chunk that
- *    starts at frame s sees a cached frame g iff g < s + chunk_frames and
- *    (g < sink_frames or g >= s - window_frames): block-causal at chunk
- *    granularity over sink + window + its own chunk.  Scores are scaled by
- *    1/sqrt(head_dim).  A query that sees no key gets O = 0, lse = -inf.
+ *    starts at frame s sees the key of a slot stamped with frame g iff
+ *    g < s + chunk_frames and (the slot is a sink slot, or
+ *    g >= s - window_frames): block-causal at chunk granularity over sink +
+ *    window + its own chunk.  Scores are scaled by 1/sqrt(head_dim).  A
+ *    query that sees no key gets O = 0, lse = -inf.
+ *  - The time position of frame g of stream b is g - offset[b]; offset[b]
+ *    starts at 0 (scv_cache_init) and grows by RoPE refreshes
+ *    (scv_rope_refresh).  Frames, stamps and slots are always global frame
+ *    indices; only the RoPE angles use time positions.
  *
  * Tensor layouts (device memory, caller-owned, 16-byte aligned, dense):
  *  q, k, v, o : [batch][n_frames*P][heads][head_dim] in the cache dtype;
@@ -166,6 +171,36 @@ scv_status scv_kv_append_roll(scv_cache* c, const void* k_rot, const void* v, co
  * (append only). */
 scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
                              const int64_t* t0, int32_t n_frames, void* stream);
+
+/* RoPE refresh (StreamDiffusionV2 review, section 2, and the gist.science
+ * StreamDiffusionV2 summary, section 2.A.2: the position offset is reset
+ * periodically so positions stay bounded on long streams).  Moves stream b's
+ * time origin forward by delta[b] frames: the time pairs of every cached key
+ * of stream b (sink and ring) are turned by -delta[b] * omega_t -- angle the
+ * fp64 product delta[b] * omega_j, cos/sin rounded to fp32, rotation in fp32,
+ * one rounding to qk_dtype -- and the stream's offset grows by delta[b], so
+ * later rotations use time position (frame - offset).  Values, stamps and
+ * slots are unchanged; attention outputs change only by rounding.
+ * delta: HOST array int64[batch], each >= 0 (0 = leave the stream alone),
+ * with the new offset below 2^40.  Later calls must keep every time position
+ * they rotate at >= 0 (SCV_E_RANGE otherwise).  Reads and writes the first
+ * ceil(d_t * elem / 16) 16-byte chunks of every key row. */
+scv_status scv_rope_refresh(scv_cache* c, const int64_t* delta, void* stream);
+
+/* Current time offsets of the streams (host int64[batch], host only). */
+scv_status scv_time_offsets(const scv_cache* c, int64_t* out);
+
+/* Sink update (StreamDiffusionV2 review, section 2, and the gist.science
+ * summary, section 2.A.2: the sink tokens are refreshed from recent
+ * content; which frames to take is the caller's choice).  Sink slot j
+ * (j < n_frames, 1 <= n_frames <= sink_frames) of stream b takes frame
+ * first_frame[b] + j: k (raw, [B][n_frames*P][H][d] in the dtype) is rotated
+ * at that frame's time position and written with v; the slot is stamped
+ * with the frame.  Ring slots and the other sink slots are untouched.  A
+ * sink slot is seen by every query chunk that does not end before its frame
+ * (no window rule).  first_frame: HOST array int64[batch]. */
+scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int64_t* first_frame, int32_t n_frames,
+                           void* stream);
 
 /* Number of key splits chunk_attention will use for this request
  * (kv_splits = 0 picks one from the device's compute-unit count; a request

@@ -82,6 +82,9 @@ _SIGNATURES = {
     "scv_rope3d_apply": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_kv_append_roll": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_rope3d_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
+    "scv_rope_refresh": (ctypes.c_int, [_VP, _I64P, _VP]),
+    "scv_time_offsets": (ctypes.c_int, [_VP, _I64P]),
+    "scv_sink_update": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_attention_splits": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32]),
     "scv_attention_workspace_bytes": (ctypes.c_size_t, [_VP, ctypes.c_int32, ctypes.c_int32]),
     "scv_chunk_attention": (
@@ -261,6 +264,27 @@ class Cache:
             self.lib.scv_rope3d_append(self.handle, _ptr(q), _ptr(q_rot), _ptr(k), _ptr(v),
                                        _t0_array(t0, self.cfg.batch), n_frames, _stream(stream)),
             "scv_rope3d_append",
+        )
+
+    def rope_refresh(self, delta, stream=None):
+        """Move each stream's time origin forward by delta[b] frames (cached
+        keys re-rotated on the device)."""
+        _check(self.lib.scv_rope_refresh(self.handle, _t0_array(delta, self.cfg.batch), _stream(stream)),
+               "scv_rope_refresh")
+
+    def time_offsets(self):
+        out = (ctypes.c_int64 * self.cfg.batch)()
+        _check(self.lib.scv_time_offsets(self.handle, out), "scv_time_offsets")
+        return [int(x) for x in out]
+
+    def sink_update(self, k, v, first_frame, n_frames, stream=None):
+        """Sink slots 0..n_frames-1 take frames first_frame[b] + j (raw k, v)."""
+        self._tok(k, n_frames, "k")
+        self._tok(v, n_frames, "v")
+        _check(
+            self.lib.scv_sink_update(self.handle, _ptr(k), _ptr(v), _t0_array(first_frame, self.cfg.batch), n_frames,
+                                     _stream(stream)),
+            "scv_sink_update",
         )
 
     def attention_splits(self, n_frames, kv_splits=0) -> int:

@@ -105,7 +105,8 @@ __device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int 
     uint64_t m = 0;
     for (int s = 0; s < g.n_slots; ++s) {
       const int64_t st = a.stamps[int64_t(b) * g.n_slots + s];
-      if (st >= 0 && st < s_c + g.C && (st < g.S_f || st >= s_c - g.W)) m |= uint64_t(1) << s;
+      // sink slots: block-causal only; ring slots: also the window
+      if (st >= 0 && st < s_c + g.C && (s < g.S_f || st >= s_c - g.W)) m |= uint64_t(1) << s;
     }
     vis_mask[threadIdx.x] = m;
   }

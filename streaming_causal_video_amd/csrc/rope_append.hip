@@ -20,6 +20,8 @@
 //  * the time-axis cos/sin of the workgroup's frame is evaluated in fp64 at
 //    workgroup start (one entry per lane), the row/column tables are static
 //    per cache and read through L1/L2.
+#include <type_traits>
+
 #include "scv_internal.h"
 
 namespace scv {
@@ -86,7 +88,14 @@ __device__ __forceinline__ void unpack16(const uint4 u, float* x) {
     x[1] = __uint_as_float(u.y);
     x[2] = __uint_as_float(u.z);
     x[3] = __uint_as_float(u.w);
-  } else {
+  } else if constexpr (std::is_same<T, _Float16>::value) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(w[i] & 0xffffu)));
+      x[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(w[i] >> 16)));
+    }
+  } else {  // bf16: the upper half of an fp32
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,6 +143,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   const int f = blockIdx.y;
   const int b = blockIdx.z;
   const int64_t gframe = a.t0[b] + f;
+  const int64_t tpos = gframe - a.pos_off[b];  // time position (after RoPE refreshes)
   const int p0 = tile * kTokTile;
   const int nvalid = min(kTokTile, g.P - p0);
   const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
@@ -146,10 +156,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   __shared__ float2 tab_t[kMaxAxisPairs];
   __shared__ uint32_t vtile[kTokTile * ROW_U32];
 
-  if (need_angles && int(threadIdx.x) < pt) tab_t[threadIdx.x] = rope_cos_sin(gframe, a.omega_t[threadIdx.x]);
+  if (need_angles && int(threadIdx.x) < pt) tab_t[threadIdx.x] = rope_cos_sin(tpos, a.omega_t[threadIdx.x]);
 
   int64_t slot = 0;
-  if (to_cache) slot = gframe < g.S_f ? gframe : g.S_f + gframe % g.R;
+  if (to_cache) slot = a.to_sink ? f : (gframe < g.S_f ? gframe : g.S_f + gframe % g.R);
 
   __syncthreads();
 
@@ -251,6 +261,61 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   if (to_cache && tile == 0 && head == 0 && threadIdx.x == 0) a.stamps[int64_t(b) * g.n_slots + slot] = gframe;
 }
 
+// RoPE refresh: every cached key row of stream b, head h (all rows_pad rows:
+// empty slots and padding rows are zero and stay zero) has its time pairs
+// turned by -delta[b] * omega_t, i.e. (x, y) -> (x c + y s, y c - x s) with
+// c, s the fp32-rounded cos/sin of the fp64 angle delta[b] * omega_j; the
+// rest of the row is untouched.  Only the 16-byte chunks that hold time dims
+// are read and written.  One workgroup = kRefreshRows rows of one (b, h).
+constexpr int kRefreshRows = 256;
+
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void rope_refresh_kernel(RefreshArgs a) {
+  constexpr int EPV = Vec16<QT>::N;
+  const Geometry& g = a.g;
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int64_t delta = a.delta[b];
+  if (delta == 0) return;  // uniform per workgroup
+  const int pt = g.dt / 2;
+  const int chunks = (g.dt + EPV - 1) / EPV;  // 16-byte chunks holding time dims
+  __shared__ float2 tab[kMaxAxisPairs];
+  if (int(threadIdx.x) < pt) tab[threadIdx.x] = rope_cos_sin(delta, a.omega_t[threadIdx.x]);
+  __syncthreads();
+  const int64_t r0 = int64_t(blockIdx.x) * kRefreshRows;
+  const int nrows = int(min<int64_t>(kRefreshRows, g.rows_pad - r0));
+  QT* base = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + r0) * D;
+  for (int i = threadIdx.x; i < nrows * chunks; i += 256) {
+    const int r = i / chunks, c = i - (i / chunks) * chunks;
+    uint4* ptr = reinterpret_cast<uint4*>(base + int64_t(r) * D + c * EPV);
+    float x[EPV];
+    unpack16<QT>(*ptr, x);
+#pragma unroll
+    for (int e = 0; e < EPV / 2; ++e) {
+      const int j = c * (EPV / 2) + e;
+      if (j < pt) {
+        const float cs = tab[j].x, sn = tab[j].y;
+        const float u = x[2 * e], v = x[2 * e + 1];
+        x[2 * e] = u * cs + v * sn;
+        x[2 * e + 1] = v * cs - u * sn;
+      }
+    }
+    *ptr = pack16<QT>(x);
+  }
+}
+
+template <typename QT, int D>
+hipError_t launch_rope_refresh_t(const RefreshArgs& a, hipStream_t s) {
+  dim3 grid(unsigned((a.g.rows_pad + kRefreshRows - 1) / kRefreshRows), a.g.H, a.g.B);
+  hipLaunchKernelGGL((rope_refresh_kernel<QT, D>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename QT>
+hipError_t launch_rope_refresh_d(const RefreshArgs& a, hipStream_t s) {
+  if (a.g.D == 128) return launch_rope_refresh_t<QT, 128>(a, s);
+  return launch_rope_refresh_t<QT, 64>(a, s);
+}
+
 template <typename T, typename QT, int D>
 hipError_t launch_rope_append_t(const RopeArgs& a, hipStream_t s) {
   const int tiles_per_frame = (a.g.P + kTokTile - 1) / kTokTile;
@@ -273,6 +338,12 @@ hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s) {
     return launch_rope_append_d<__bf16, __bf16>(a, s);
   }
   return launch_rope_append_d<float, float>(a, s);
+}
+
+hipError_t launch_rope_refresh(const RefreshArgs& a, hipStream_t s) {
+  if (a.g.qk_dtype == SCV_FP16) return launch_rope_refresh_d<_Float16>(a, s);
+  if (a.g.qk_dtype == SCV_BF16) return launch_rope_refresh_d<__bf16>(a, s);
+  return launch_rope_refresh_d<float>(a, s);
 }
 
 hipError_t launch_rope_tables(const Geometry& g, const Omegas& om, const int64_t* t0, int32_t n_frames, float* out_t,

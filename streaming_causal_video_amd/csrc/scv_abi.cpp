@@ -14,6 +14,10 @@ struct scv_cache {
   scv::Omegas om;
   scv_cache_layout lay;
   char* base;
+  // Time position of frame g of stream b is g - pos_off[b]; RoPE refreshes
+  // move it forward, cache_init resets it.  Host state, updated in call
+  // order (a cache is used by one stream at a time).
+  int64_t pos_off[scv::kMaxBatch];
 };
 
 namespace {
@@ -147,6 +151,18 @@ scv_status check_times(const scv_cache* c, const int64_t* t0, int32_t n_frames) 
   return SCV_OK;
 }
 
+// Time positions t0[b] - pos_off[b] .. + n_frames - 1 must stay in [0, 2^40).
+scv_status check_positions(const scv_cache* c, const int64_t* t0, int32_t n_frames) {
+  for (int b = 0; b < c->g.B; ++b) {
+    const int64_t p = t0[b] - c->pos_off[b];
+    if (p < 0 || p > scv::kMaxTime - n_frames)
+      return fail(SCV_E_RANGE, "stream " + std::to_string(b) + ": frame " + std::to_string(t0[b]) +
+                                   " has time position " + std::to_string(p) + " after RoPE refreshes of " +
+                                   std::to_string(c->pos_off[b]) + " frames; positions must lie in [0, 2^40)");
+  }
+  return SCV_OK;
+}
+
 scv_status check_ptr(const void* p, const char* name, bool required) {
   if (!p) {
     if (required) return fail(SCV_E_INVALID, std::string(name) + " is NULL");
@@ -179,7 +195,10 @@ scv::RopeArgs base_rope_args(const scv_cache* c, const int64_t* t0, int32_t n_fr
   std::memset(&a, 0, sizeof(a));
   a.g = c->g;
   a.n_frames = n_frames;
-  for (int b = 0; b < c->g.B; ++b) a.t0[b] = t0[b];
+  for (int b = 0; b < c->g.B; ++b) {
+    a.t0[b] = t0[b];
+    a.pos_off[b] = c->pos_off[b];
+  }
   for (int j = 0; j < c->g.dt / 2; ++j) a.omega_t[j] = c->om.t[j];
   a.tab_h = reinterpret_cast<const float2*>(c->base + c->lay.table_h_offset);
   a.tab_w = reinterpret_cast<const float2*>(c->base + c->lay.table_w_offset);
@@ -319,6 +338,7 @@ scv_status scv_cache_init(scv_cache* c, const void* sink_k, const void* sink_v, 
     if ((s = check_ptr(sink_k, "sink_k", false)) != SCV_OK) return s;
     if ((s = check_ptr(sink_v, "sink_v", false)) != SCV_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int b = 0; b < c->g.B; ++b) c->pos_off[b] = 0;
     if ((s = hip_status(scv::launch_cache_reset(c->g, c->base + c->lay.k_offset, c->lay.total_bytes - c->lay.k_offset,
                                                 reinterpret_cast<int64_t*>(c->base + c->lay.stamps_offset), st),
                         "cache reset launch")) != SCV_OK)
@@ -353,6 +373,7 @@ scv_status scv_rope3d_apply(const scv_cache* c, void* q, void* k, const int64_t*
     if (n_frames < 1 || n_frames > 65535 || int64_t(n_frames) * c->g.P >= (int64_t(1) << 31))
       return fail(SCV_E_SHAPE, "n_frames must be in [1, 65535] with n_frames * P < 2^31");
     if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
+    if ((s = check_positions(c, t0, n_frames)) != SCV_OK) return s;
     scv::RopeArgs a = base_rope_args(c, t0, n_frames);
     a.q_in = q;
     a.q_out = q;
@@ -397,6 +418,7 @@ scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const voi
     if ((s = check_ptr(v, "v", true)) != SCV_OK) return s;
     if ((s = check_times(c, t0, n_frames < 1 ? 1 : n_frames)) != SCV_OK) return s;
     if ((s = check_append_frames(c, t0, n_frames)) != SCV_OK) return s;
+    if ((s = check_positions(c, t0, n_frames)) != SCV_OK) return s;
     scv::RopeArgs a = base_rope_args(c, t0, n_frames);
     set_cache_targets(c, &a);
     a.q_in = q;
@@ -405,6 +427,71 @@ scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const voi
     a.v_in = v;
     a.rotate_k = 1;
     return hip_status(scv::launch_rope_append(a, static_cast<hipStream_t>(stream)), "rope3d_append launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_rope_refresh(scv_cache* c, const int64_t* delta, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if (!delta) return fail(SCV_E_INVALID, "delta is NULL");
+    bool any = false;
+    for (int b = 0; b < c->g.B; ++b) {
+      if (delta[b] < 0 || delta[b] >= scv::kMaxTime - c->pos_off[b])
+        return fail(SCV_E_RANGE, "delta[" + std::to_string(b) + "] = " + std::to_string(delta[b]) +
+                                     " must be >= 0 and keep the stream's offset below 2^40");
+      any = any || delta[b] != 0;
+    }
+    if (!any) return SCV_OK;
+    scv::RefreshArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.g = c->g;
+    a.cache_k = c->base + c->lay.k_offset;
+    for (int b = 0; b < c->g.B; ++b) a.delta[b] = delta[b];
+    for (int j = 0; j < c->g.dt / 2; ++j) a.omega_t[j] = c->om.t[j];
+    if ((s = hip_status(scv::launch_rope_refresh(a, static_cast<hipStream_t>(stream)), "rope_refresh launch")) !=
+        SCV_OK)
+      return s;
+    for (int b = 0; b < c->g.B; ++b) c->pos_off[b] += delta[b];
+    return SCV_OK;
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_time_offsets(const scv_cache* c, int64_t* out) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if (!out) return fail(SCV_E_INVALID, "out is NULL");
+    for (int b = 0; b < c->g.B; ++b) out[b] = c->pos_off[b];
+    return SCV_OK;
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int64_t* first_frame, int32_t n_frames,
+                           void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((s = check_ptr(k, "k", true)) != SCV_OK) return s;
+    if ((s = check_ptr(v, "v", true)) != SCV_OK) return s;
+    if (c->g.S_f < 1) return fail(SCV_E_SHAPE, "the cache has no sink slots (sink_frames == 0)");
+    if (n_frames < 1 || n_frames > c->g.S_f)
+      return fail(SCV_E_SHAPE, "n_frames must be in [1, sink_frames = " + std::to_string(c->g.S_f) + "]");
+    if ((s = check_times(c, first_frame, n_frames)) != SCV_OK) return s;
+    if ((s = check_positions(c, first_frame, n_frames)) != SCV_OK) return s;
+    scv::RopeArgs a = base_rope_args(c, first_frame, n_frames);
+    set_cache_targets(c, &a);
+    a.k_in = k;
+    a.v_in = v;
+    a.rotate_k = 1;
+    a.to_sink = 1;
+    return hip_status(scv::launch_rope_append(a, static_cast<hipStream_t>(stream)), "sink_update launch");
   } catch (...) {
     return fail(SCV_E_INVALID, "internal error");
   }
@@ -505,12 +592,15 @@ scv_status scv_rope_tables(const scv_cache* c, const int64_t* t0, int32_t n_fram
     if ((s = check_ptr(out, "out", true)) != SCV_OK) return s;
     if (n_frames < 1 || n_frames > 65535) return fail(SCV_E_SHAPE, "n_frames must be in [1, 65535]");
     if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
+    if ((s = check_positions(c, t0, n_frames)) != SCV_OK) return s;
     const size_t need = scv_rope_table_floats(c, n_frames);
     if (n_floats < need) return fail(SCV_E_SHAPE, "out holds fewer than " + std::to_string(need) + " floats");
     const size_t nt = size_t(c->g.B) * n_frames * (c->g.dt / 2);
     const size_t nh = size_t(c->g.grid_h) * (c->g.dh / 2);
     float2* base = reinterpret_cast<float2*>(out);
-    return hip_status(scv::launch_rope_tables(c->g, c->om, t0, n_frames, out, base + nt, base + nt + nh,
+    int64_t pos[scv::kMaxBatch];
+    for (int b = 0; b < c->g.B; ++b) pos[b] = t0[b] - c->pos_off[b];
+    return hip_status(scv::launch_rope_tables(c->g, c->om, pos, n_frames, out, base + nt, base + nt + nh,
                                               static_cast<hipStream_t>(stream)),
                       "rope table launch");
   } catch (...) {

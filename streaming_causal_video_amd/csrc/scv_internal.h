@@ -52,8 +52,19 @@ struct RopeArgs {
   const float2* tab_w;
   int32_t n_frames;
   int32_t rotate_k;  // 0: k is already rotated (kv_append_roll)
+  int32_t to_sink;   // 1: frame f of the call goes to sink slot f (sink update)
   Geometry g;
-  int64_t t0[kMaxBatch];
+  int64_t t0[kMaxBatch];       // global frame of the call's first frame
+  int64_t pos_off[kMaxBatch];  // time position = global frame - pos_off
+  double omega_t[kMaxAxisPairs];
+};
+
+// RoPE refresh arguments (by value): turn the time pairs of every cached
+// key of stream b by -delta[b] * omega_t.
+struct RefreshArgs {
+  void* cache_k;
+  Geometry g;
+  int64_t delta[kMaxBatch];
   double omega_t[kMaxAxisPairs];
 };
 
@@ -97,6 +108,7 @@ inline int attn_rows_per_workgroup(const Geometry& g) {
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
 hipError_t launch_rope_tables(const Geometry& g, const Omegas& om, const int64_t* t0, int32_t n_frames,
                               float* out_t, float2* out_h, float2* out_w, hipStream_t s);
+hipError_t launch_rope_refresh(const RefreshArgs& a, hipStream_t s);
 hipError_t launch_cache_reset(const Geometry& g, void* kv_base, size_t kv_bytes, int64_t* stamps, hipStream_t s);
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t s);

@@ -212,3 +212,33 @@ def test_last_error_is_set(lib):
     assert lib.scv_rope3d_apply(h, None, None, t0(5), 3, None) == -1
     assert "NULL" in B.last_error()
     lib.scv_cache_destroy(h)
+
+
+def test_refresh_validation(lib):
+    cfg, h = make_handle(lib, batch=2)
+    off = (ctypes.c_int64 * 2)()
+    assert lib.scv_time_offsets(h, off) == 0 and list(off) == [0, 0]
+    assert lib.scv_time_offsets(h, None) == -1
+    assert lib.scv_rope_refresh(None, t0(1, 1), None) == -1
+    assert lib.scv_rope_refresh(h, None, None) == -1
+    assert lib.scv_rope_refresh(h, t0(3, -1), None) == -5
+    assert lib.scv_rope_refresh(h, t0(1 << 40, 0), None) == -5
+    # all-zero deltas: nothing to do, nothing enqueued, offsets unchanged
+    assert lib.scv_rope_refresh(h, t0(0, 0), None) == 0
+    assert lib.scv_time_offsets(h, off) == 0 and list(off) == [0, 0]
+    lib.scv_cache_destroy(h)
+
+
+def test_sink_update_validation(lib):
+    cfg, h = make_handle(lib, sink_frames=2, window_frames=11)
+    k = FAKE + (1 << 36)
+    assert lib.scv_sink_update(h, None, k, t0(7), 1, None) == -1
+    assert lib.scv_sink_update(h, k, k + 4, t0(7), 1, None) == -4
+    assert lib.scv_sink_update(h, k, k, t0(7), 0, None) == -2
+    assert lib.scv_sink_update(h, k, k, t0(7), 3, None) == -2  # more frames than sink slots
+    assert lib.scv_sink_update(h, k, k, t0(-1), 1, None) == -5
+    assert lib.scv_sink_update(h, k, k, None, 1, None) == -1
+    lib.scv_cache_destroy(h)
+    cfg, h = make_handle(lib, sink_frames=0, window_frames=13)
+    assert lib.scv_sink_update(h, k, k, t0(7), 1, None) == -2  # no sink slots
+    lib.scv_cache_destroy(h)
