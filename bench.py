@@ -149,8 +149,9 @@ def time_refresh_and_sink(r, w, reps=20):
     first = list(w.t0)
     res = {}
     for name, fn, nbytes in (
-        ("rope_refresh", lambda: r.cache.rope_refresh([1] * B), refresh_bytes),
+        # the sink update first: the refreshes move time positions below t0
         ("sink_update", lambda: r.cache.sink_update(k1, v1, first, 1), sink_bytes),
+        ("rope_refresh", lambda: r.cache.rope_refresh([1] * B), refresh_bytes),
     ):
         fn()
         torch.cuda.synchronize()

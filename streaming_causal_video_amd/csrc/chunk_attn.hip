@@ -30,6 +30,8 @@
 //  * Optional key splits write normalised fp32 partials + lse, combined by
 //    attn_merge (lse-weighted).
 // An fp32 instantiation (v_mfma_f32_32x32x2_f32) follows the same structure.
+#include <type_traits>
+
 #include "scv_internal.h"
 
 namespace scv {
@@ -64,13 +66,24 @@ constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Frame-slot visibility masks per query chunk, the workgroup's union and
-// intersection, and per-key classification.
-struct Visibility {
-  uint64_t any;  // slots some query of the workgroup may see
-  uint64_t all;  // slots every query of the workgroup may see
-  uint64_t mine; // slots this lane's query may see
+// Query tiles never straddle two query chunks: tile i of chunk c covers rows
+// [c * rows_per_chunk + i * ROWS, ...) up to the end of the chunk.  Every
+// query of a workgroup therefore sees the same frame slots.
+struct QueryTile {
+  int chunk;
+  int row_lo;   // first query row
+  int row_end;  // one past the last query row (<= row_lo when the tile is empty)
 };
+
+template <int ROWS_PER_WG>
+__device__ __forceinline__ QueryTile query_tile(const AttnArgs& a, int qtile) {
+  QueryTile q;
+  q.chunk = qtile / a.qtiles_per_chunk;
+  const int i = qtile - q.chunk * a.qtiles_per_chunk;
+  q.row_lo = q.chunk * a.rows_per_chunk + i * ROWS_PER_WG;
+  q.row_end = min(min(q.row_lo + ROWS_PER_WG, (q.chunk + 1) * a.rows_per_chunk), a.Nq);
+  return q;
+}
 
 __device__ __forceinline__ uint64_t tile_slot_bits(const Geometry& g, int t) {
   const int64_t r0 = int64_t(t) * kKeyTile;
@@ -81,48 +94,45 @@ __device__ __forceinline__ uint64_t tile_slot_bits(const Geometry& g, int t) {
   return hi & ~((uint64_t(1) << s_lo) - 1);
 }
 
-// Branch-free per-key visibility (rows < 2^31: at most 64 slots of <= 2^20
-// rows).  Evaluated with bitwise ands and applied with a select, so no
-// per-element divergent branch reaches the accumulator registers.
-__device__ __forceinline__ bool key_visible(const Geometry& g, uint64_t mask, int row) {
-  const int slot_rows = int(g.slot_rows);
-  const int slot = row / slot_rows;
-  const int p = row - slot * slot_rows;
-  const uint32_t in_rows = row < int(g.rows);
-  const uint32_t in_slot = p < g.P;
-  const uint32_t seen = uint32_t(mask >> (slot & 63)) & 1u;
-  return (in_rows & in_slot & seen) != 0;
+// Frame slots the queries of chunk `chunk` of stream b may see: lane s of
+// every wave tests slot s (n_slots <= 64) and a ballot gathers the mask, so
+// the result is a wave-uniform scalar without a trip through LDS.  A sink
+// slot is seen when its frame does not lie after the chunk (block-causal
+// only); a ring slot also needs its frame inside the window.
+__device__ __forceinline__ uint64_t chunk_slot_mask(const AttnArgs& a, int b, int chunk) {
+  const Geometry& g = a.g;
+  const int s = threadIdx.x & 63;
+  const int64_t s_c = a.t0[b] + int64_t(chunk) * g.C;
+  bool seen = false;
+  if (s < g.n_slots) {
+    const int64_t st = a.stamps[int64_t(b) * g.n_slots + s];
+    seen = st >= 0 && st < s_c + g.C && (s < g.S_f || st >= s_c - g.W);
+  }
+  return __ballot(seen);
 }
 
-template <int ROWS_PER_WG>
-__device__ __forceinline__ Visibility compute_visibility(const AttnArgs& a, int b, int qtile, int qrow, bool qvalid,
-                                                         uint64_t* vis_mask) {
-  const Geometry& g = a.g;
-  const int n_chunks = (a.n_frames + g.C - 1) / g.C;
-  const int64_t t0 = a.t0[b];
-  if (int(threadIdx.x) < n_chunks) {
-    const int64_t s_c = t0 + int64_t(threadIdx.x) * g.C;
-    uint64_t m = 0;
-    for (int s = 0; s < g.n_slots; ++s) {
-      const int64_t st = a.stamps[int64_t(b) * g.n_slots + s];
-      // sink slots: block-causal only; ring slots: also the window
-      if (st >= 0 && st < s_c + g.C && (s < g.S_f || st >= s_c - g.W)) m |= uint64_t(1) << s;
+// Visible keys of tile t as a 64-bit mask (bit r = key row r0 + r): rows of
+// visible slots that hold tokens (slot padding and rows past the last slot
+// excluded).  Scalar work, done only for tiles that are not fully visible.
+__device__ __forceinline__ uint64_t tile_key_mask(const Geometry& g, uint64_t slots, int t) {
+  const int r0 = t * kKeyTile;
+  const int sr = int(g.slot_rows);
+  const int rows = int(g.rows);
+  uint64_t m = 0;
+  int s = r0 / sr;
+  for (int base = s * sr; base < r0 + kKeyTile && base < rows; base += sr, ++s) {
+    if ((slots >> s) & 1) {
+      const int lo = max(base, r0) - r0;
+      const int hi = min(min(base + g.P, r0 + kKeyTile), rows) - r0;
+      if (hi > lo) m |= (hi - lo == 64 ? ~uint64_t(0) : ((uint64_t(1) << (hi - lo)) - 1)) << lo;
     }
-    vis_mask[threadIdx.x] = m;
   }
-  __syncthreads();
-  const int rows_per_chunk = g.P * g.C;
-  const int row_lo = qtile * ROWS_PER_WG;
-  const int row_hi = min(row_lo + ROWS_PER_WG, a.Nq) - 1;
-  Visibility v;
-  v.any = 0;
-  v.all = ~uint64_t(0);
-  for (int c = row_lo / rows_per_chunk; c <= row_hi / rows_per_chunk; ++c) {
-    v.any |= vis_mask[c];
-    v.all &= vis_mask[c];
-  }
-  v.mine = vis_mask[qvalid ? qrow / rows_per_chunk : row_lo / rows_per_chunk];
-  return v;
+  return m;
+}
+
+// Is every key row of tile t visible under the slot mask?
+__device__ __forceinline__ bool tile_full(const Geometry& g, uint64_t slots, int t) {
+  return ((tile_slot_bits(g, t) & ~slots) == 0) && (int64_t(t + 1) * kKeyTile <= g.rows) && (g.slot_rows == g.P);
 }
 
 // ---------------------------------------------------------------------------
@@ -186,21 +196,50 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
 }
 
 // Workgroups are handed to the 8 XCDs of the chip round robin by linear
-// index, each XCD with its own L2.  Renumber them so that every XCD runs a
-// contiguous range of (query tile fastest, then head, then stream/split):
-// the query tiles of one head then share that head's K/V in one L2 instead
-// of each XCD fetching it from HBM.
+// index, each XCD with its own L2.  The work items -- (query chunk fastest,
+// then query tile, then head, then stream/split) -- are renumbered so that
+// every XCD runs a contiguous range of them: the query tiles of one head
+// then share that head's K/V in one L2 instead of each XCD fetching it from
+// HBM, and with several query chunks every XCD gets the same mix of chunks.
+// Inside its range an XCD takes later chunks first: a later chunk sees at
+// least as many keys, so the longest workgroups start first.
 constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_remap(int* x, int* y, int* z) {
+struct WorkItem {
+  int qtile;  // chunk * qtiles_per_chunk + tile in chunk
+  int head;
+  int bz;     // stream * splits + split
+};
+__device__ __forceinline__ WorkItem attn_work_item(const AttnArgs& a) {
   const int nx = gridDim.x, ny = gridDim.y;
   const int n = nx * ny * gridDim.z;
   const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
   const int xcd = id % kXcds, k = id / kXcds;
   const int base = n / kXcds, extra = n % kXcds;  // XCDs below `extra` run one more
-  const int logical = xcd * base + min(xcd, extra) + k;
-  *x = logical % nx;
-  *y = (logical / nx) % ny;
-  *z = logical / (nx * ny);
+  const int lo = xcd * base + min(xcd, extra);
+  const int cnt = base + (xcd < extra ? 1 : 0);
+  const int nch = a.n_qtiles / a.qtiles_per_chunk;
+  // k-th item of the range in descending chunk order
+  int p = k;
+  {
+    int before = 0;
+    for (int c = nch - 1; c >= 0; --c) {
+      const int r = ((c - lo) % nch + nch) % nch;  // first position of chunk c in the range
+      const int m = r < cnt ? (cnt - r + nch - 1) / nch : 0;
+      if (k < before + m) {
+        p = r + nch * (k - before);
+        break;
+      }
+      before += m;
+    }
+  }
+  const int logical = lo + p;
+  const int chunk = logical % nch;
+  const int rest = logical / nch;
+  WorkItem w;
+  w.qtile = chunk * a.qtiles_per_chunk + rest % a.qtiles_per_chunk;
+  w.head = (rest / a.qtiles_per_chunk) % ny;
+  w.bz = rest / (a.qtiles_per_chunk * ny);
+  return w;
 }
 
 // LDS row r of a K tile holds key row kperm(r) of the tile.
@@ -269,13 +308,13 @@ struct TileWalk {
     const uint64_t hi = shi >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (shi + 1)) - 1);
     return hi & ~((uint64_t(1) << slo) - 1);
   }
-  // advance to the next tile some query of the workgroup may see (from the
-  // cursor itself when `first`); returns t_end when there is none
-  __device__ __forceinline__ int next(const Geometry& g, const Visibility& v, bool first, bool* full) {
+  // advance to the next tile with a visible key (from the cursor itself when
+  // `first`); returns t_end when there is none
+  __device__ __forceinline__ int next(const Geometry& g, uint64_t slots, bool first, bool* full) {
     if (!first) step(g);
-    while (t < t_end && (bits(g) & v.any) == 0) step(g);
+    while (t < t_end && (bits(g) & slots) == 0) step(g);
     if (t >= t_end) return t_end;
-    *full = ((bits(g) & ~v.all) == 0) && (r0 + kKeyTile <= int(g.rows)) && (g.slot_rows == g.P);
+    *full = ((bits(g) & ~slots) == 0) && (r0 + kKeyTile <= int(g.rows)) && (g.slot_rows == g.P);
     return t;
   }
 };
@@ -288,20 +327,22 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = T::KS, DB = T::DB;
 
   __shared__ __attribute__((aligned(1024))) char smem[kStages * T::STAGE];
-  __shared__ uint64_t vis_mask[kMaxQueryChunks];
 
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lead = wave < 4;  // MFMA phase first
   const int hl = lane >> 5, l32 = lane & 31;
-  int qtile, head, bz;
-  xcd_remap(&qtile, &head, &bz);
+  const WorkItem wi = attn_work_item(a);
+  const int head = wi.head, bz = wi.bz;
+  const QueryTile qt = query_tile<kRowsBf16>(a, wi.qtile);
+  if (qt.row_lo >= qt.row_end) return;  // an empty tile of a partial last chunk
   const int b = bz / a.splits, split = bz % a.splits;
-  const int qrow = qtile * kRowsBf16 + wave * 32 + l32;
-  const bool qvalid = qrow < a.Nq;
+  const int qrow = qt.row_lo + wave * 32 + l32;
+  const bool qvalid = qrow < qt.row_end;
 
-  const Visibility vis = compute_visibility<kRowsBf16>(a, b, qtile, qrow, qvalid, vis_mask);
+  // frame slots every query of this workgroup may see (wave-uniform)
+  const uint64_t slots = chunk_slot_mask(a, b, qt.chunk);
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, a.tiles_total);
@@ -369,8 +410,6 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   float msc_run = 0.f;                 // m_run * c (0 while m_run is -inf)
   const float c = a.scale_log2;
   constexpr float kPBound = 1024.f;    // largest exponential kept (2^10)
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   floatx16 s[2];      // S^T of a tile: keys 32j .. 32j+31 (in kperm order) x this wave's 32 queries
   bf16x8 p[2][2];     // P^T of a tile: [half j][16-key group gg]
@@ -419,16 +458,18 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     pv_ops(st);
     interleave(4 * DB);
   };
-  // element i of s[j] in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4)
+  // Masks the keys of tile t that no query here may see.  Element i of s[j]
+  // in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4) of the tile, that
+  // is key 32j + 16(a>>1) + 8hl + 4(a&1) + i%4 with a = i/4.
   auto mask = [&](int t) {
-    const int r0 = t * kKeyTile;
-    const uint64_t mine = vis.mine;
+    const uint64_t km = tile_key_mask(g, slots, t) >> (8 * hl);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = r0 + 32 * j + kperm(8 * (i / 4) + 4 * hl + (i & 3));
-        s[j][i] = key_visible(g, mine, key) ? s[j][i] : -INFINITY;
+        const int a4 = i / 4;
+        const int bit = 32 * j + 16 * (a4 >> 1) + 4 * (a4 & 1) + (i & 3);
+        s[j][i] = ((km >> bit) & 1) ? s[j][i] : -INFINITY;
       }
   };
   // Exponentials of s against the reference offset msc, rounded to bf16 into
@@ -486,13 +527,12 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     l_run += rs[0] + rs[1];
   };
 
-  // Pass 1 -- the fully visible tiles (all of them in steady state).  With
-  // tile i in LDS stage i % 4, each trip of the loop first publishes tile i
-  // (everyone's loads of it have landed) and starts the load of tile i + 2
-  // into the stage of tile i - 2, which every wave finished in the previous
-  // trip.  Online softmax does not depend on key order, so the partially
-  // visible tiles are taken afterwards (pass 2) and this loop carries no
-  // masking code.
+  // The key loop over every tile with a visible key.  With tile i in LDS
+  // stage i % 4, each trip first publishes tile i (everyone's loads of it
+  // have landed) and starts the load of tile i + 2 into the stage of tile
+  // i - 2, which every wave finished in the previous trip.  Tiles that are
+  // only partly visible (slot padding, window edges, the row tail) have
+  // their hidden keys masked before the softmax.
   TileWalk walk;
   walk.init(g, t_begin, t_end);
   // every tile of the split fully visible (the steady state): no walk needed
@@ -501,20 +541,22 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     const int s_lo = int((int64_t(t_begin) * kKeyTile) / g.slot_rows);
     const int s_hi = int((int64_t(t_end) * kKeyTile - 1) / g.slot_rows);
     const uint64_t hi = s_hi >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (s_hi + 1)) - 1);
-    dense = ((hi & ~((uint64_t(1) << s_lo) - 1)) & ~vis.all) == 0;
+    dense = ((hi & ~((uint64_t(1) << s_lo) - 1)) & ~slots) == 0;
   }
-  int dense_t = t_begin - 1;
-  auto next_full = [&](bool first) {
-    if (dense) {
-      dense_t = first ? t_begin : dense_t + 1;
-      return dense_t < t_end ? dense_t : t_end;
-    }
-    bool full = false;
-    int t = walk.next(g, vis, first, &full);
-    while (t < t_end && !full) t = walk.next(g, vis, false, &full);
-    return t;
-  };
-  {
+  // One key loop, instantiated twice: without any masking code when every
+  // tile of the split is fully visible, and with masks otherwise.
+  auto key_loop = [&](auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    int dense_t = t_begin - 1;
+    auto next_tile = [&](bool first, bool* full) {
+      if constexpr (!kMasked) {
+        dense_t = first ? t_begin : dense_t + 1;
+        *full = true;
+        return dense_t < t_end ? dense_t : t_end;
+      } else {
+        return walk.next(g, slots, first, full);
+      }
+    };
     // Slots between barriers: the lead waves (0-3) run, for tile i, the MFMA
     // phase M(i) (P V of tile i-1, S^T of tile i) in one slot and the softmax
     // V(i) in the next; the other waves (4-7) pass one extra barrier first,
@@ -524,8 +566,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     // the barrier that starts the wave's trip) as its M(i) starts; tile i+1
     // is waited for before the barrier that ends the lead waves' V(i), which
     // publishes it.  Every wave passes the same number of barriers.
-    int tq0 = next_full(true);                        // tile i
-    int tq1 = tq0 < t_end ? next_full(false) : t_end;  // tile i + 1
+    bool f0 = true, f1 = true;                              // fully visible?
+    int tq0 = next_tile(true, &f0);                         // tile i
+    int tq1 = tq0 < t_end ? next_tile(false, &f1) : t_end;  // tile i + 1
     if (tq0 < t_end) {
       issue_tile(tq0, 0);
       if (tq1 < t_end) {
@@ -541,6 +584,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       while (true) {
         const bool cur = tq0 < t_end;
         int tq2 = t_end;
+        bool f2 = true;
         auto wait_next = [&]() {
           if (tq1 < t_end) {
             if (tq2 < t_end)
@@ -550,7 +594,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
           }
         };
         if (tq1 < t_end) {
-          tq2 = next_full(false);
+          tq2 = next_tile(false, &f2);
           if (tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
         }
         // M(i)
@@ -563,41 +607,29 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         if (!lead) wait_next();
         __syncthreads();
         // V(i)
-        if (cur) softmax();
+        if (cur) {
+          if constexpr (kMasked) {
+            if (!f0) mask(tq0);
+          }
+          softmax();
+        }
         if (lead) wait_next();
         __syncthreads();
         if (!cur) break;
         have_prev = true;
         tq0 = tq1;
+        f0 = f1;
         tq1 = tq2;
+        f1 = f2;
         si = (si + 1) % kStages;
       }
       if (lead) __syncthreads();
     }
-  }
-
-  // Pass 2 -- partially visible tiles (warm-up, slot padding, the row tail),
-  // one at a time with per-key masks.
-  if (!dense) {
-    TileWalk pw;
-    pw.init(g, t_begin, t_end);
-    bool first = true;
-    while (true) {
-      bool full = true;
-      int tp = pw.next(g, vis, first, &full);
-      first = false;
-      while (tp < t_end && full) tp = pw.next(g, vis, false, &full);
-      if (tp >= t_end) break;
-      __syncthreads();  // every wave is done with stage 0
-      issue_tile(tp, 0);
-      wait_vm<0>();
-      __syncthreads();
-      qk(smem);
-      mask(tp);
-      softmax();
-      pv(smem);
-    }
-  }
+  };
+  if (dense)
+    key_loop(std::false_type{});
+  else
+    key_loop(std::true_type{});
 
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -652,21 +684,22 @@ __global__ __launch_bounds__(256) void chunk_attn_f32_kernel(AttnArgs a) {
   static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile sizes");
 
   __shared__ __attribute__((aligned(16))) char smem[2][KBYTES + D * VROW];
-  __shared__ uint64_t vis_mask[kMaxQueryChunks];
 
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
-  const int qtile = blockIdx.x, head = blockIdx.y;
+  const int head = blockIdx.y;
+  const QueryTile qt = query_tile<kBlockM>(a, a.n_qtiles - 1 - int(blockIdx.x));
+  if (qt.row_lo >= qt.row_end) return;  // an empty tile of a partial last chunk
   const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
-  const int qrow = qtile * kBlockM + wave * 32 + l32;
-  const bool qvalid = qrow < a.Nq;
+  const int qrow = qt.row_lo + wave * 32 + l32;
+  const bool qvalid = qrow < qt.row_end;
 
-  const Visibility vis = compute_visibility<kBlockM>(a, b, qtile, qrow, qvalid, vis_mask);
+  const uint64_t slots = chunk_slot_mask(a, b, qt.chunk);
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, a.tiles_total);
   auto next_tile = [&](int t) {
-    while (t < t_end && (tile_slot_bits(g, t) & vis.any) == 0) ++t;
+    while (t < t_end && (tile_slot_bits(g, t) & slots) == 0) ++t;
     return t;
   };
 
@@ -731,15 +764,14 @@ __global__ __launch_bounds__(256) void chunk_attn_f32_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[e], qf[m][e], s[kb], 0, 0, 0);
       }
     }
-    const int64_t r0 = int64_t(t) * kKeyTile;
-    const bool full = ((tile_slot_bits(g, t) & ~vis.all) == 0) && (r0 + kKeyTile <= g.rows) && (g.slot_rows == g.P);
-    if (!full) {
-      const int r0i = int(r0);
+    if (!tile_full(g, slots, t)) {
+      // element i of s[kb] in lane half hl is key 32kb + 8(i/4) + 4hl + i%4
+      const uint64_t km = tile_key_mask(g, slots, t) >> (4 * hl);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          s[kb][i] = key_visible(g, vis.mine, r0i + 32 * kb + 8 * (i / 4) + 4 * hl + (i & 3)) ? s[kb][i] : -INFINITY;
+          s[kb][i] = ((km >> (32 * kb + 8 * (i / 4) + (i & 3))) & 1) ? s[kb][i] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll

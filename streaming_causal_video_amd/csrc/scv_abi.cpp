@@ -228,11 +228,17 @@ int device_cu_count() {
 int resolve_splits(const scv_cache* c, int32_t n_frames, int32_t requested) {
   const int tiles = int(c->g.rows_pad / scv::kKeyTile);
   if (requested > 0) return std::max(1, std::min(std::min(requested, tiles), 64));
-  const int64_t nq = int64_t(n_frames) * c->g.P;
   const int rows = scv::attn_rows_per_workgroup(c->g);
-  const int64_t qtiles = (nq + rows - 1) / rows;
+  const int64_t nq = int64_t(n_frames) * c->g.P;
+  const int64_t rows_per_chunk = std::min<int64_t>(int64_t(c->g.C) * c->g.P, nq);
+  const int64_t qtiles = ((n_frames + c->g.C - 1) / c->g.C) * ((rows_per_chunk + rows - 1) / rows);
   const int64_t wgs = qtiles * c->g.H * c->g.B;
   const int cus = device_cu_count();
+  // Key tiles a workgroup visits: a query chunk sees at most the sink, the
+  // window and its own chunk (the steady state; fewer near the stream start),
+  // wherever the ring has put them.
+  const int64_t seen_frames = std::min<int64_t>(c->g.n_slots, int64_t(c->g.S_f) + c->g.W + c->g.C);
+  const int64_t vis_tiles = std::min<int64_t>(tiles, (seen_frames * c->g.slot_rows + scv::kKeyTile - 1) / scv::kKeyTile + 1);
   // Estimated makespan in units of one workgroup-tile: rounds of workgroups
   // over the compute units, each round as long as one split's key tiles
   // plus a fixed start/drain cost of 3 tiles; with splits, the fp32
@@ -242,7 +248,9 @@ int resolve_splits(const scv_cache* c, int32_t n_frames, int32_t requested) {
   double best = 0.0;
   int best_s = 1;
   for (int s = 1; s <= std::min(64, tiles); ++s) {
-    const int64_t per = (tiles + s - 1) / s;
+    // the longest split: with several chunks (or a window not covering the
+    // whole ring) some chunk may see all of one split's tiles
+    const int64_t per = std::min<int64_t>(vis_tiles, (tiles + s - 1) / s);
     const int64_t rounds = (wgs * s + cus - 1) / cus;
     double cost = double(rounds) * double(per + 3);
     if (s > 1) cost += 2.0 + 2.0 * rows_total * s * (4.0 * c->g.D + 4.0) / 24e6;
@@ -547,7 +555,12 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
     a.stamps = reinterpret_cast<const int64_t*>(c->base + c->lay.stamps_offset);
     a.n_frames = n_frames;
     a.Nq = n_frames * c->g.P;
-    a.n_qtiles = (a.Nq + scv::attn_rows_per_workgroup(c->g) - 1) / scv::attn_rows_per_workgroup(c->g);
+    {
+      const int rows_wg = scv::attn_rows_per_workgroup(c->g);
+      a.rows_per_chunk = c->g.C * c->g.P;
+      a.qtiles_per_chunk = (std::min(a.rows_per_chunk, a.Nq) + rows_wg - 1) / rows_wg;
+      a.n_qtiles = ((n_frames + c->g.C - 1) / c->g.C) * a.qtiles_per_chunk;
+    }
     a.splits = splits;
     a.tiles_total = int32_t(c->g.rows_pad / scv::kKeyTile);
     a.tiles_per_split = (a.tiles_total + splits - 1) / splits;

@@ -80,7 +80,9 @@ struct AttnArgs {
   const int64_t* stamps;
   int32_t n_frames;
   int32_t Nq;             // n_frames * P query rows per stream
-  int32_t n_qtiles;
+  int32_t n_qtiles;       // n_chunks * qtiles_per_chunk
+  int32_t qtiles_per_chunk;  // query tiles never straddle two query chunks
+  int32_t rows_per_chunk;    // chunk_frames * P
   int32_t splits;
   int32_t tiles_total;    // rows_pad / kKeyTile
   int32_t tiles_per_split;

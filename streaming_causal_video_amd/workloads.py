@@ -135,8 +135,33 @@ WAN13B_720P = WAN13B_480P.with_(
     description="720p 1.3B-shaped layer: 3600 tokens/frame, 10800 queries, 43200 keys, t0=20000",
 )
 
-WORKLOADS = {w.name: w for w in (TINY_FP32, WAN13B_480P, WAN13B_480P_B4, WAN14B_480P, WAN13B_720P)}
-ORDERED = [TINY_FP32, WAN13B_480P, WAN13B_480P_B4, WAN14B_480P, WAN13B_720P]
+# Several query chunks in one call (ring R = W + 4*C = 24 frames).  The first
+# frames of a stream (time to first frame): chunks of frames 0-2, 3-5, 6-8,
+# 9-11, each block-causal over everything before it, 4680 .. 18720 keys.
+WAN13B_480P_PREFILL = WAN13B_480P.with_(
+    name="wan1.3b-480p-prefill",
+    max_query_chunks=4,
+    t0=(0,),
+    seed=6,
+    description="480p first frames in one call: 4 chunks of 3 frames from t0=0 (block-causal triangle, "
+    "4680..18720 keys per chunk)",
+)
+
+# Four consecutive chunks of the steady state in one call: each sees the
+# sink, the 12 frames before its own start and itself (24960 keys), a window
+# that slides by 3 frames from chunk to chunk.
+WAN13B_480P_CHUNKS4 = WAN13B_480P.with_(
+    name="wan1.3b-480p-chunks4",
+    max_query_chunks=4,
+    t0=(1000,),
+    seed=7,
+    description="480p, 4 consecutive chunks of 3 frames in one call at t0=1000 (18720 queries, "
+    "24960 keys each over a sliding window)",
+)
+
+ORDERED = [TINY_FP32, WAN13B_480P, WAN13B_480P_B4, WAN14B_480P, WAN13B_720P, WAN13B_480P_PREFILL,
+           WAN13B_480P_CHUNKS4]
+WORKLOADS = {w.name: w for w in ORDERED}
 
 
 def fill_schedule(w: Workload):

@@ -47,6 +47,8 @@ def test_layout_of_workloads(lib):
         "wan1.3b-480p-stream4": (16, 1560, 24960, 24960),
         "wan14b-480p": (16, 1560, 24960, 24960),
         "wan1.3b-720p": (12, 3600, 43200, 43200),
+        "wan1.3b-480p-prefill": (25, 1560, 39000, 39040),
+        "wan1.3b-480p-chunks4": (25, 1560, 39000, 39040),
     }
     for w in W.ORDERED:
         cfg = B.config_for(w)
