@@ -271,50 +271,59 @@ struct Bf16Tile {
   static __device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 };
 
-// Division-free walk over the key tiles of a split: for the tile under the
-// cursor it tracks the frame slots of its first and last row, so that the
-// visibility of each tile costs a few scalar operations.
-struct TileWalk {
+// Walk over the key tiles of a split [t_begin, t_end) that hold a key of a
+// visible slot, one run of consecutive visible slots at a time: inside a run
+// the next tile is t + 1 and whether it is fully visible is a range test, so
+// the loop pays a few scalar operations per tile; opening the next run costs
+// a couple of bit scans.  Tiles come out in increasing order; a tile shared
+// by two runs (a run gap shorter than a tile) is visited once, and its mask
+// covers both runs.
+struct RunWalk {
   int t, t_end;
-  int r0, slo, slo_end, shi, shi_end;  // first row; slot of first/last row; row after each slot
+  int last;     // last tile of the current run (clipped to the split)
+  int ff, fu;   // tiles ff .. fu of the run hold visible keys only
+  int s_next;   // first slot after the current run
+  bool exact;   // slot_rows == P: no padding rows inside a run
+  bool valid;
 
-  __device__ __forceinline__ void init(const Geometry& g, int t_begin, int t_end_) {
-    t = t_begin;
+  // Opens the first run at or after slot from_slot with a tile >= min_t.
+  __device__ __forceinline__ bool open(const Geometry& g, uint64_t slots, int from_slot, int min_t) {
+    while (from_slot < g.n_slots) {
+      const uint64_t m = slots & (~uint64_t(0) << from_slot);
+      if (m == 0) return false;
+      const int s0 = __builtin_ctzll(m);
+      const uint64_t inv = ~slots & (~uint64_t(0) << s0);
+      const int s1 = min(inv ? int(__builtin_ctzll(inv)) : 64, g.n_slots);
+      const int sr = int(g.slot_rows);
+      const int r_lo = s0 * sr, r_hi = (s1 - 1) * sr + g.P;  // rows of the run's tokens
+      last = min((r_hi - 1) >> 6, t_end - 1);
+      ff = (r_lo + kKeyTile - 1) >> 6;
+      fu = (r_hi >> 6) - 1;
+      s_next = s1;
+      t = max(r_lo >> 6, min_t);
+      if (t >= t_end) return false;
+      if (t <= last) return true;
+      from_slot = s1;
+    }
+    return false;
+  }
+  __device__ __forceinline__ void init(const Geometry& g, uint64_t slots, int t_begin, int t_end_) {
     t_end = t_end_;
-    r0 = t * kKeyTile;
-    const int sr = int(g.slot_rows);
-    slo = r0 / sr;
-    slo_end = (slo + 1) * sr;
-    const int r1 = min(r0 + kKeyTile - 1, int(g.rows) - 1);
-    shi = r1 / sr;
-    shi_end = (shi + 1) * sr;
+    exact = g.slot_rows == g.P;
+    valid = t_begin < t_end && open(g, slots, int((int64_t(t_begin) * kKeyTile) / g.slot_rows), t_begin);
   }
-  __device__ __forceinline__ void step(const Geometry& g) {
-    const int sr = int(g.slot_rows);
-    ++t;
-    r0 += kKeyTile;
-    while (r0 >= slo_end) {
-      ++slo;
-      slo_end += sr;
-    }
-    const int r1 = min(r0 + kKeyTile - 1, int(g.rows) - 1);
-    while (r1 >= shi_end) {
-      ++shi;
-      shi_end += sr;
-    }
-  }
-  __device__ __forceinline__ uint64_t bits(const Geometry& g) const {
-    if (r0 >= int(g.rows)) return 0;
-    const uint64_t hi = shi >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (shi + 1)) - 1);
-    return hi & ~((uint64_t(1) << slo) - 1);
-  }
-  // advance to the next tile with a visible key (from the cursor itself when
-  // `first`); returns t_end when there is none
+  // the next tile with a visible key (the first one when `first`); t_end when
+  // there is none
   __device__ __forceinline__ int next(const Geometry& g, uint64_t slots, bool first, bool* full) {
-    if (!first) step(g);
-    while (t < t_end && (bits(g) & slots) == 0) step(g);
-    if (t >= t_end) return t_end;
-    *full = ((bits(g) & ~slots) == 0) && (r0 + kKeyTile <= int(g.rows)) && (g.slot_rows == g.P);
+    if (first) {
+      if (!valid) return t_end;
+    } else if (t < last) {
+      ++t;
+    } else if (!open(g, slots, s_next, t + 1)) {
+      t = t_end;
+      return t_end;
+    }
+    *full = exact ? (t >= ff && t <= fu) : tile_full(g, slots, t);
     return t;
   }
 };
@@ -533,8 +542,8 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   // i - 2, which every wave finished in the previous trip.  Tiles that are
   // only partly visible (slot padding, window edges, the row tail) have
   // their hidden keys masked before the softmax.
-  TileWalk walk;
-  walk.init(g, t_begin, t_end);
+  RunWalk walk;
+  walk.init(g, slots, t_begin, t_end);
   // every tile of the split fully visible (the steady state): no walk needed
   bool dense = false;
   if (t_begin < t_end && int64_t(t_end) * kKeyTile <= g.rows && g.slot_rows == g.P) {
