@@ -202,13 +202,20 @@ scv_status scv_time_offsets(const scv_cache* c, int64_t* out);
 scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int64_t* first_frame, int32_t n_frames,
                            void* stream);
 
-/* Number of key splits chunk_attention will use for this request
- * (kv_splits = 0 picks one from the device's compute-unit count; a request
- * is capped at 64 and at the number of 64-key tiles). */
-int32_t scv_attention_splits(const scv_cache* c, int32_t n_frames, int32_t kv_splits);
+/* Number of key splits chunk_attention will use for this request.
+ * kv_splits > 0 asks for that many (capped at 64 and at the number of 64-key
+ * tiles).  kv_splits = 0 lets a makespan model choose from the device's
+ * compute-unit count: with t0 (HOST int64[batch], nullable) it counts the
+ * keys each stream's chunks can see; with t0 = NULL it assumes every chunk
+ * sees sink + window + chunk (the steady state).  Only split counts whose
+ * workspace fits ws_bytes are considered (SIZE_MAX: no limit). */
+int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
+                             size_t ws_bytes);
 
-/* Workspace bytes chunk_attention needs for this request (0 when it runs
- * without splits). */
+/* Workspace bytes chunk_attention needs for this request with
+ * kv_splits > 0, or the most the steady-state choice of kv_splits = 0 needs
+ * (0 when it runs without splits).  With kv_splits = 0, chunk_attention
+ * picks among the split counts this workspace (and t0) allows. */
 size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits);
 
 /* chunk_attention(q, cache) -> o.  Block-causal attention of the rotated
@@ -219,7 +226,8 @@ size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32
  * (qk_dtype operands for QK^T; dtype operands for PV), softmax in fp32; P is
  * rounded to the dtype before PV.  With more
  * than one split each split writes normalised fp32 partials into ws and a
- * merge kernel combines them (lse-weighted). */
+ * merge kernel combines them (lse-weighted).  kv_splits = 0 chooses as
+ * scv_attention_splits(c, t0, n_frames, 0, ws ? ws_bytes : 0) does. */
 scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
                                float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream);
 

@@ -85,7 +85,7 @@ _SIGNATURES = {
     "scv_rope_refresh": (ctypes.c_int, [_VP, _I64P, _VP]),
     "scv_time_offsets": (ctypes.c_int, [_VP, _I64P]),
     "scv_sink_update": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
-    "scv_attention_splits": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32]),
+    "scv_attention_splits": (ctypes.c_int32, [_VP, _I64P, ctypes.c_int32, ctypes.c_int32, ctypes.c_size_t]),
     "scv_attention_workspace_bytes": (ctypes.c_size_t, [_VP, ctypes.c_int32, ctypes.c_int32]),
     "scv_chunk_attention": (
         ctypes.c_int,
@@ -287,8 +287,12 @@ class Cache:
             "scv_sink_update",
         )
 
-    def attention_splits(self, n_frames, kv_splits=0) -> int:
-        return int(self.lib.scv_attention_splits(self.handle, n_frames, kv_splits))
+    def attention_splits(self, n_frames, kv_splits=0, t0=None, ws_bytes=None) -> int:
+        """Splits chunk_attention uses (t0: the request's start frames or None
+        for the steady-state estimate; ws_bytes: the workspace it will get)."""
+        t = None if t0 is None else _t0_array(t0, self.cfg.batch)
+        lim = (1 << 64) - 1 if ws_bytes is None else int(ws_bytes)
+        return int(self.lib.scv_attention_splits(self.handle, t, n_frames, kv_splits, lim))
 
     def workspace_bytes(self, n_frames, kv_splits=0) -> int:
         return int(self.lib.scv_attention_workspace_bytes(self.handle, n_frames, kv_splits))

@@ -197,12 +197,13 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
 
 // Workgroups are handed to the 8 XCDs of the chip round robin by linear
 // index, each XCD with its own L2.  The work items -- (query chunk fastest,
-// then query tile, then head, then stream/split) -- are renumbered so that
+// then stream/split, then query tile, then head) -- are renumbered so that
 // every XCD runs a contiguous range of them: the query tiles of one head
 // then share that head's K/V in one L2 instead of each XCD fetching it from
-// HBM, and with several query chunks every XCD gets the same mix of chunks.
-// Inside its range an XCD takes later chunks first: a later chunk sees at
-// least as many keys, so the longest workgroups start first.
+// HBM, and every XCD gets the same mix of chunks and streams (which differ in
+// length near a stream's start).  Inside its range an XCD takes later chunks
+// first: a later chunk sees at least as many keys, so the longest
+// workgroups start first.
 constexpr int kXcds = 8;
 struct WorkItem {
   int qtile;  // chunk * qtiles_per_chunk + tile in chunk
@@ -233,12 +234,14 @@ __device__ __forceinline__ WorkItem attn_work_item(const AttnArgs& a) {
     }
   }
   const int logical = lo + p;
+  const int nz = gridDim.z;
   const int chunk = logical % nch;
   const int rest = logical / nch;
+  const int rest2 = rest / nz;
   WorkItem w;
-  w.qtile = chunk * a.qtiles_per_chunk + rest % a.qtiles_per_chunk;
-  w.head = (rest / a.qtiles_per_chunk) % ny;
-  w.bz = rest / (a.qtiles_per_chunk * ny);
+  w.bz = rest % nz;
+  w.qtile = chunk * a.qtiles_per_chunk + rest2 % a.qtiles_per_chunk;
+  w.head = rest2 / a.qtiles_per_chunk;
   return w;
 }
 

@@ -2,6 +2,7 @@
 // cache layout, per-cache constants and kernel launches.  Every entry point
 // validates before enqueueing anything and never lets an exception escape.
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -225,35 +226,61 @@ int device_cu_count() {
   return cached[dev];
 }
 
-int resolve_splits(const scv_cache* c, int32_t n_frames, int32_t requested) {
+size_t workspace_bytes(const scv_cache* c, int32_t n_frames, int splits);
+
+// Frames a query chunk starting at frame s_c can see once its history is in
+// the cache: the sink frames before its end, and the window + chunk frames.
+int64_t seen_frames(const scv_cache* c, int64_t s_c) {
+  const int64_t end = s_c + c->g.C;
+  const int64_t sink = std::min<int64_t>(c->g.S_f, std::max<int64_t>(end, 0));
+  const int64_t lo = std::max<int64_t>(c->g.S_f, s_c - c->g.W);
+  return std::min<int64_t>(c->g.n_slots, sink + std::max<int64_t>(0, end - lo));
+}
+
+// Key splits for a request.  kv_splits > 0 is taken as given (capped at 64
+// and at the tile count).  Otherwise a makespan model picks one: workgroups
+// of each (stream, chunk) class visit their visible key tiles (from t0 when
+// given, else the steady state), split s ways -- a split may hold up to all
+// of a class's tiles, at most tiles/s of them; they run in rounds over the
+// compute units, each round as long as the longest workgroup plus a fixed
+// 3-tile start/drain cost; with splits the fp32 partials are written and
+// read back by the merge (at ~8.5 MB per tile-time, plus 2 tile-times for
+// the extra launch).  Only split counts whose workspace fits ws_limit count.
+int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t requested, size_t ws_limit) {
   const int tiles = int(c->g.rows_pad / scv::kKeyTile);
   if (requested > 0) return std::max(1, std::min(std::min(requested, tiles), 64));
   const int rows = scv::attn_rows_per_workgroup(c->g);
   const int64_t nq = int64_t(n_frames) * c->g.P;
   const int64_t rows_per_chunk = std::min<int64_t>(int64_t(c->g.C) * c->g.P, nq);
-  const int64_t qtiles = ((n_frames + c->g.C - 1) / c->g.C) * ((rows_per_chunk + rows - 1) / rows);
-  const int64_t wgs = qtiles * c->g.H * c->g.B;
+  const int n_chunks = (n_frames + c->g.C - 1) / c->g.C;
+  const int64_t per_class = ((rows_per_chunk + rows - 1) / rows) * c->g.H;  // workgroups per (stream, chunk)
   const int cus = device_cu_count();
-  // Key tiles a workgroup visits: a query chunk sees at most the sink, the
-  // window and its own chunk (the steady state; fewer near the stream start),
-  // wherever the ring has put them.
-  const int64_t seen_frames = std::min<int64_t>(c->g.n_slots, int64_t(c->g.S_f) + c->g.W + c->g.C);
-  const int64_t vis_tiles = std::min<int64_t>(tiles, (seen_frames * c->g.slot_rows + scv::kKeyTile - 1) / scv::kKeyTile + 1);
-  // Estimated makespan in units of one workgroup-tile: rounds of workgroups
-  // over the compute units, each round as long as one split's key tiles
-  // plus a fixed start/drain cost of 3 tiles; with splits, the fp32
-  // partials are written and merged (their HBM bytes at ~24 MB per unit,
-  // plus 2 units for the extra launch).
+  constexpr int kMaxClasses = scv::kMaxBatch * scv::kMaxQueryChunks;
+  int64_t len[kMaxClasses];
+  int n_cls = 0;
+  for (int b = 0; b < (t0 ? c->g.B : 1); ++b)
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      const int64_t f = t0 ? seen_frames(c, t0[b] + int64_t(ch) * c->g.C)
+                           : std::min<int64_t>(c->g.n_slots, int64_t(c->g.S_f) + c->g.W + c->g.C);
+      len[n_cls++] = std::min<int64_t>(tiles, (f * c->g.slot_rows + scv::kKeyTile - 1) / scv::kKeyTile + 1);
+    }
+  const int64_t class_mult = t0 ? 1 : c->g.B;  // without t0 every stream is one steady-state class
   const double rows_total = double(nq) * c->g.H * c->g.B;
+  const double merge_unit = 2.0 * rows_total * (4.0 * c->g.D + 4.0) / 8.5e6;
   double best = 0.0;
   int best_s = 1;
   for (int s = 1; s <= std::min(64, tiles); ++s) {
-    // the longest split: with several chunks (or a window not covering the
-    // whole ring) some chunk may see all of one split's tiles
-    const int64_t per = std::min<int64_t>(vis_tiles, (tiles + s - 1) / s);
-    const int64_t rounds = (wgs * s + cus - 1) / cus;
-    double cost = double(rounds) * double(per + 3);
-    if (s > 1) cost += 2.0 + 2.0 * rows_total * s * (4.0 * c->g.D + 4.0) / 24e6;
+    if (s > 1 && workspace_bytes(c, n_frames, s) > ws_limit) break;
+    const int64_t cap = (tiles + s - 1) / s;
+    double work = 0.0, lmax = 0.0;
+    for (int i = 0; i < n_cls; ++i) {
+      const double per = double(std::min<int64_t>(len[i], cap)) + 3.0;
+      work += double(per_class * class_mult * s) * per;
+      lmax = std::max(lmax, per);
+    }
+    const double rounds = std::ceil(work / (double(cus) * lmax) - 1e-9);
+    double cost = rounds * lmax;
+    if (s > 1) cost += 2.0 + s * merge_unit;
     if (s == 1 || cost < best) {
       best = cost;
       best_s = s;
@@ -505,10 +532,12 @@ scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int
   }
 }
 
-int32_t scv_attention_splits(const scv_cache* c, int32_t n_frames, int32_t kv_splits) {
+int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
+                             size_t ws_bytes) {
   try {
     if (!c || n_frames < 1 || kv_splits < 0) return 0;
-    return resolve_splits(c, n_frames, kv_splits);
+    if (t0 && check_times(c, t0, n_frames) != SCV_OK) return 0;
+    return resolve_splits(c, t0, n_frames, kv_splits, ws_bytes);
   } catch (...) {
     return 0;
   }
@@ -517,7 +546,7 @@ int32_t scv_attention_splits(const scv_cache* c, int32_t n_frames, int32_t kv_sp
 size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits) {
   try {
     if (!c || n_frames < 1 || kv_splits < 0) return 0;
-    return workspace_bytes(c, n_frames, resolve_splits(c, n_frames, kv_splits));
+    return workspace_bytes(c, n_frames, resolve_splits(c, nullptr, n_frames, kv_splits, SIZE_MAX));
   } catch (...) {
     return 0;
   }
@@ -535,7 +564,8 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
       return fail(SCV_E_SHAPE, "n_frames must be in [1, max_query_chunks*chunk_frames]");
     if (kv_splits < 0) return fail(SCV_E_INVALID, "kv_splits must be >= 0");
     if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
-    const int splits = resolve_splits(c, n_frames, kv_splits);
+    // with kv_splits = 0 the choice sees t0 and the workspace given
+    const int splits = resolve_splits(c, t0, n_frames, kv_splits, ws ? ws_bytes : 0);
     const size_t need = workspace_bytes(c, n_frames, splits);
     if (need > 0) {
       if (!ws) return fail(SCV_E_WORKSPACE, "workspace is NULL; need " + std::to_string(need) + " bytes");

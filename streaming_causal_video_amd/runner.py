@@ -43,7 +43,8 @@ class StreamRunner:
         self.lse = torch.empty((w.batch, w.heads, nq * w.tokens_per_frame), dtype=torch.float32, device=device) \
             if with_lse else None
         self.ws = self.cache.make_workspace(nq, kv_splits)
-        self.splits = self.cache.attention_splits(nq, kv_splits)
+        ws_bytes = 0 if self.ws is None else self.ws.numel()
+        self.splits = self.cache.attention_splits(nq, kv_splits, t0=w.t0, ws_bytes=ws_bytes)
 
     def fill(self, stream=None):
         """cache_init with the sink frames, then the window frames."""

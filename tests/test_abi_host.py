@@ -185,14 +185,14 @@ def test_attention_validation(lib):
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -1, None, 0, None) == -1
     need = lib.scv_attention_workspace_bytes(h, 3, 4)
     assert need > 0
-    assert lib.scv_attention_splits(h, 3, 4) == 4
+    assert lib.scv_attention_splits(h, None, 3, 4, (1 << 64) - 1) == 4
     assert lib.scv_attention_workspace_bytes(h, 3, 1) == 0
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, 4, None, 0, None) == -7
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, 4, q, need - 1, None) == -7
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, 4, q + 16, need, None) == -4
     assert lib.scv_chunk_attention(h, q, t0(-5), 3, q, None, 4, q, need, None) == -5
     # the split request is capped by the tile count and by 64
-    assert lib.scv_attention_splits(h, 3, 1000) == 64
+    assert lib.scv_attention_splits(h, None, 3, 1000, (1 << 64) - 1) == 64
     lib.scv_cache_destroy(h)
 
 
@@ -243,4 +243,18 @@ def test_sink_update_validation(lib):
     lib.scv_cache_destroy(h)
     cfg, h = make_handle(lib, sink_frames=0, window_frames=13)
     assert lib.scv_sink_update(h, k, k, t0(7), 1, None) == -2  # no sink slots
+    lib.scv_cache_destroy(h)
+
+
+def test_auto_splits_respect_workspace_and_t0(lib):
+    # 720p, one stream: the steady-state choice splits; without workspace it
+    # cannot; a stream at t0 = 0 sees only its own chunk
+    cfg, h = make_handle(lib, grid_h=45, grid_w=80, window_frames=8)
+    big = (1 << 64) - 1
+    s_steady = lib.scv_attention_splits(h, None, 3, 0, big)
+    assert s_steady > 1
+    assert lib.scv_attention_workspace_bytes(h, 3, 0) > 0
+    assert lib.scv_attention_splits(h, None, 3, 0, 0) == 1
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, big) == s_steady
+    assert lib.scv_attention_splits(h, t0(-1), 3, 0, big) == 0
     lib.scv_cache_destroy(h)
