@@ -51,7 +51,11 @@ Readings taken where they are silent (each also listed in the design doc):
   frame first[b] + j -- its k rotated at that frame's own time position, its
   v, and the frame as stamp -- and the ring is not touched; R19 a key in a
   sink slot is seen by every query chunk that ends after its frame (no
-  window rule), a key in a ring slot by R7/R8.
+  window rule), a key in a ring slot by R7/R8; R20 the QKV projection that
+  the pages fuse with RoPE ([CausalRoPE] 2(c)) is a plain linear map without
+  bias or normalisation: q, k, v = x W_q^T, x W_k^T, x W_v^T with one weight
+  [3*H*d, d_model] whose rows are the q features, then k, then v (feature
+  h*d + i = dim i of head h).
 
 Pinned by tests/test_oracle_*.py (brute force, closed forms, the RoPE
 relative-position invariant, torch SDPA in float64, rolling-cache == masked
@@ -77,6 +81,7 @@ __all__ = [
     "slot_visible",
     "attention",
     "merge_partials",
+    "qkv_project",
     "OracleCache",
     "full_history_attention",
 ]
@@ -279,6 +284,18 @@ def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
 
 
 # --------------------------------------------------------------------------
+# QKV projection   ([CausalRoPE] 2(c): fused with RoPE into one kernel)
+# --------------------------------------------------------------------------
+def qkv_project(x: np.ndarray, w_qkv: np.ndarray, heads: int, head_dim: int):
+    """q, k, v [B, N, H, d] of the layer input x [B, N, d_model] under the
+    weight w_qkv [3*H*d, d_model] (reading R20), in fp64."""
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w_qkv, dtype=np.float64).T
+    B, N = y.shape[:2]
+    y = y.reshape(B, N, 3, heads, head_dim)
+    return y[:, :, 0], y[:, :, 1], y[:, :, 2]
+
+
+# --------------------------------------------------------------------------
 # the cache, following the four calls of the boundary
 # --------------------------------------------------------------------------
 class OracleCache:
@@ -336,6 +353,12 @@ class OracleCache:
         """Fused form: returns q rotated, appends rotated k and v."""
         self.kv_append_roll(self.rope3d_apply(k, t0, n_frames), v, t0, n_frames)
         return self.rope3d_apply(q, t0, n_frames)
+
+    def qkv_rope_append(self, x, w_qkv, t0, n_frames):
+        """Projection of the layer input followed by rope3d_append
+        ([CausalRoPE] 2(c)); returns q rotated."""
+        q, k, v = qkv_project(x, w_qkv, self.spec.heads, self.spec.head_dim)
+        return self.rope3d_append(q, k, v, t0, n_frames)
 
     # RoPE refresh ([SDV2-blog] 2; [SDV2-summary] 2.A.2) -------------------
     def rope_refresh(self, delta: Sequence[int]):

@@ -15,7 +15,7 @@ from collections import OrderedDict
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_K_OUTLIER = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_K_OUTLIER, TENSOR_X, TENSOR_W = 0, 1, 2, 3, 4, 5
 
 
 def _gen(seed: int, stream: int, tensor: int, frame: int) -> np.random.Generator:
@@ -87,3 +87,24 @@ def frames_tensor(w, tensor: int, t0, n_frames: int) -> np.ndarray:
         for f in range(n_frames):
             out[b, f * P : (f + 1) * P] = frame_tensor(w, tensor, b, int(t0[b]) + f)
     return out
+
+
+def hidden_frames(w, d_model: int, t0, n_frames: int) -> np.ndarray:
+    """Layer input (hidden states) of frames t0[b] .. t0[b]+n_frames-1:
+    [B, n*P, d_model] fp64, N(0, 1) draws rounded to the dtype."""
+    P = w.tokens_per_frame
+    out = np.empty((w.batch, n_frames * P, d_model))
+    for b in range(w.batch):
+        for f in range(n_frames):
+            x = _gen(w.seed, b, TENSOR_X, int(t0[b]) + f).standard_normal((P, d_model))
+            out[b, f * P : (f + 1) * P] = round_dtype(x, w.dtype)
+    return out
+
+
+def qkv_weight(w, d_model: int) -> np.ndarray:
+    """Projection weight [3*H*d, d_model] (rows: q features, then k, then v;
+    feature h*d + i is dim i of head h): N(0, 1/d_model) draws (unit-variance
+    outputs for unit-variance inputs) rounded to the dtype."""
+    n_out = 3 * w.heads * w.head_dim
+    x = _gen(w.seed, 0, TENSOR_W, 0).standard_normal((n_out, d_model)) / np.sqrt(d_model)
+    return round_dtype(x, w.dtype)

@@ -542,6 +542,41 @@ def check_sink_update_with_the_sink_itself_is_a_no_op():
         assert np.array_equal(a.stamps, b.stamps)
 
 
+# ------------------------------------------------------- QKV projection ---
+def check_qkv_projection_brute_force():
+    """Triple loops over (token, output feature, input feature), with the
+    feature order written out: q head h dim i is weight row h*d + i, k the
+    same after H*d rows, v after 2*H*d rows."""
+    rng = np.random.default_rng(71)
+    B, N, Dm, H, d = 2, 3, 5, 2, 4
+    x = rng.standard_normal((B, N, Dm))
+    w = rng.standard_normal((3 * H * d, Dm))
+    q, k, v = O.qkv_project(x, w, H, d)
+    for b in range(B):
+        for n in range(N):
+            for h in range(H):
+                for i in range(d):
+                    for which, out in enumerate((q, k, v)):
+                        row = which * H * d + h * d + i
+                        want = sum(x[b, n, c] * w[row, c] for c in range(Dm))
+                        assert abs(out[b, n, h, i] - want) <= 1e-12, (which, b, n, h, i)
+
+
+def check_qkv_projection_selects_columns():
+    """A weight of one-hot rows copies the chosen input features exactly."""
+    rng = np.random.default_rng(72)
+    B, N, Dm, H, d = 1, 4, 7, 1, 2
+    x = rng.standard_normal((B, N, Dm))
+    pick = [3, 0, 6, 6, 1, 2]  # input feature of each of the 3*H*d rows
+    w = np.zeros((3 * H * d, Dm))
+    for r, c in enumerate(pick):
+        w[r, c] = 1.0
+    q, k, v = O.qkv_project(x, w, H, d)
+    assert np.array_equal(q[0, :, 0], x[0][:, [3, 0]])
+    assert np.array_equal(k[0, :, 0], x[0][:, [6, 6]])
+    assert np.array_equal(v[0, :, 0], x[0][:, [1, 2]])
+
+
 ALL_CHECKS = [
     check_golden_unit_vectors,
     check_frequency_ladder,
@@ -564,4 +599,6 @@ ALL_CHECKS = [
     check_refresh_equals_rotation_at_earlier_time,
     check_sink_update_brute_force,
     check_sink_update_with_the_sink_itself_is_a_no_op,
+    check_qkv_projection_brute_force,
+    check_qkv_projection_selects_columns,
 ]

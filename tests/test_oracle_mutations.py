@@ -13,6 +13,7 @@ _orig_rope3d = O.rope3d
 _orig_attention = O.attention
 _orig_frame_visible = O.frame_visible
 _orig_frame_slot = O.frame_slot
+_orig_qkv = O.qkv_project
 
 
 def _rope3d_variant(sign=1.0, half_split=False, order=(0, 1, 2)):
@@ -111,6 +112,29 @@ def _sink_update_at_slot_time(self, k, v, first_frame, n_frames):
             self.stamps[b, j] = int(first_frame[b]) + j
 
 
+def _qkv_transposed(x, w):
+    # reads the weight as [d_model, 3*H*d] in memory order (a transposed operand)
+    wt = np.asarray(w).reshape(-1)[: w.size].reshape(w.shape[1], w.shape[0])
+    return np.asarray(x) @ wt
+
+
+def _split(y, x, H, d):
+    y = y.reshape(x.shape[0], x.shape[1], 3, H, d)
+    return y[:, :, 0], y[:, :, 1], y[:, :, 2]
+
+
+def _qkv_swapped(x, w, H, d):
+    q, k, v = _orig_qkv(x, w, H, d)
+    return q, v, k
+
+
+def _qkv_interleaved(x, w, H, d):
+    # features taken as (head, q/k/v, dim) instead of (q/k/v, head, dim)
+    y = np.asarray(x) @ np.asarray(w).T
+    y = y.reshape(x.shape[0], x.shape[1], H, 3, d)
+    return y[:, :, :, 0], y[:, :, :, 1], y[:, :, :, 2]
+
+
 MUTATIONS = {
     "rope_sin_sign": ("rope3d", _rope3d_variant(sign=-1.0)),
     "rope_half_split_pairs": ("rope3d", _rope3d_variant(half_split=True)),
@@ -139,6 +163,9 @@ MUTATIONS = {
     "sink_follows_window": ("slot_visible", lambda slot, g, s, C, sf, W: O.frame_visible(g, s, C, sf, W)),
     "sink_not_causal": ("slot_visible", lambda slot, g, s, C, sf, W: g >= 0 if slot < sf else
                         O.frame_visible(g, s, C, sf, W)),
+    "qkv_weight_not_transposed": ("qkv_project", lambda x, w, H, d: _split(_qkv_transposed(x, w), x, H, d)),
+    "qkv_k_v_swapped": ("qkv_project", lambda x, w, H, d: _qkv_swapped(x, w, H, d)),
+    "qkv_heads_interleaved": ("qkv_project", lambda x, w, H, d: _qkv_interleaved(x, w, H, d)),
     "merge_unweighted": (
         "merge_partials",
         lambda o, l: (np.asarray(o).mean(axis=0), np.logaddexp.reduce(np.asarray(l), axis=0)),
