@@ -172,6 +172,21 @@ scv_status scv_kv_append_roll(scv_cache* c, const void* k_rot, const void* v, co
 scv_status scv_rope3d_append(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
                              const int64_t* t0, int32_t n_frames, void* stream);
 
+/* QKV projection fused with 3D RoPE and the append (Causal-RoPE SP paper,
+ * section 2(c): the projection and Causal-RoPE run as one kernel).  For the
+ * layer input x ([B][n_frames*P][d_model], dtype SCV_BF16 only) of frames
+ * t0[b] .. t0[b]+n_frames-1 and the weight w_qkv ([3*H*d][d_model]: rows
+ * 0 .. H*d-1 are the q features, feature h*d + i being dim i of head h, then
+ * the k features, then the v features), computes q, k, v = x w^T with fp32
+ * accumulation (no bias, no normalisation), rotates q into q_rot
+ * ([B][n_frames*P][H][d], qk_dtype) and k into the cache, writes v into the
+ * cache and stamps the slots -- the same result as scv_rope3d_append on the
+ * projected q, k, v, except that q, k and v are rounded once, after RoPE.
+ * d_model: a multiple of 32 in [32, 65536], with n_frames*P*d_model*2 < 2^31.
+ * Frame rules as for scv_kv_append_roll. */
+scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, const void* w_qkv, void* q_rot,
+                               const int64_t* t0, int32_t n_frames, void* stream);
+
 /* RoPE refresh (StreamDiffusionV2 review, section 2, and the gist.science
  * StreamDiffusionV2 summary, section 2.A.2: the position offset is reset
  * periodically so positions stay bounded on long streams).  Moves stream b's

@@ -82,6 +82,7 @@ _SIGNATURES = {
     "scv_rope3d_apply": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_kv_append_roll": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_rope3d_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
+    "scv_qkv_rope_append": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_rope_refresh": (ctypes.c_int, [_VP, _I64P, _VP]),
     "scv_time_offsets": (ctypes.c_int, [_VP, _I64P]),
     "scv_sink_update": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
@@ -264,6 +265,24 @@ class Cache:
             self.lib.scv_rope3d_append(self.handle, _ptr(q), _ptr(q_rot), _ptr(k), _ptr(v),
                                        _t0_array(t0, self.cfg.batch), n_frames, _stream(stream)),
             "scv_rope3d_append",
+        )
+
+    def qkv_rope_append(self, x, w_qkv, q_rot, t0, n_frames, stream=None):
+        """Projection of the layer input x [B, n*P, d_model] by w_qkv
+        [3*H*d, d_model], with RoPE and the cache append fused in."""
+        c = self.cfg
+        d_model = int(x.shape[-1]) if x is not None else 0
+        want_x = (c.batch, n_frames * self.P, d_model)
+        if x is None or tuple(x.shape) != want_x or x.dtype != self.dtype or not x.is_contiguous():
+            raise ValueError(f"x: need contiguous {self.dtype} tensor {want_x}")
+        want_w = (3 * c.heads * c.head_dim, d_model)
+        if w_qkv is None or tuple(w_qkv.shape) != want_w or w_qkv.dtype != self.dtype or not w_qkv.is_contiguous():
+            raise ValueError(f"w_qkv: need contiguous {self.dtype} tensor {want_w}")
+        self._tok(q_rot, n_frames, "q_rot", rotated=True)
+        _check(
+            self.lib.scv_qkv_rope_append(self.handle, _ptr(x), d_model, _ptr(w_qkv), _ptr(q_rot),
+                                         _t0_array(t0, c.batch), n_frames, _stream(stream)),
+            "scv_qkv_rope_append",
         )
 
     def rope_refresh(self, delta, stream=None):

@@ -27,14 +27,6 @@
 namespace scv {
 namespace {
 
-// cos/sin of the fp64 angle pos * omega, rounded to fp32 (round to nearest).
-__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, double omega) {
-  const double th = static_cast<double>(pos) * omega;
-  double s, c;
-  sincos(th, &s, &c);
-  return make_float2(static_cast<float>(c), static_cast<float>(s));
-}
-
 struct TableArgs {
   Geometry g;
   Omegas om;

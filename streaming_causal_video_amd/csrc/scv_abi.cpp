@@ -532,6 +532,47 @@ scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int
   }
 }
 
+scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, const void* w_qkv, void* q_rot,
+                               const int64_t* t0, int32_t n_frames, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if (c->g.dtype != SCV_BF16) return fail(SCV_E_DTYPE, "the fused projection needs dtype SCV_BF16");
+    if ((s = check_ptr(x, "x", true)) != SCV_OK) return s;
+    if ((s = check_ptr(w_qkv, "w_qkv", true)) != SCV_OK) return s;
+    if ((s = check_ptr(q_rot, "q_rot", true)) != SCV_OK) return s;
+    if (d_model < 32 || d_model % 32 != 0 || d_model > 65536)
+      return fail(SCV_E_SHAPE, "d_model must be a multiple of 32 in [32, 65536]");
+    if ((s = check_times(c, t0, n_frames < 1 ? 1 : n_frames)) != SCV_OK) return s;
+    if ((s = check_append_frames(c, t0, n_frames)) != SCV_OK) return s;
+    if ((s = check_positions(c, t0, n_frames)) != SCV_OK) return s;
+    if (3 * int64_t(c->g.H) > 65535) return fail(SCV_E_SHAPE, "the fused projection supports at most 21845 heads");
+    if (int64_t(n_frames) * c->g.P * d_model * 2 >= (int64_t(1) << 31))
+      return fail(SCV_E_SHAPE, "n_frames * P * d_model * 2 bytes must stay below 2^31 per stream");
+    scv::QkvArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.w = w_qkv;
+    a.q_out = q_rot;
+    a.cache_k = c->base + c->lay.k_offset;
+    a.cache_v = c->base + c->lay.v_offset;
+    a.stamps = reinterpret_cast<int64_t*>(c->base + c->lay.stamps_offset);
+    a.tab_h = reinterpret_cast<const float2*>(c->base + c->lay.table_h_offset);
+    a.tab_w = reinterpret_cast<const float2*>(c->base + c->lay.table_w_offset);
+    a.d_model = d_model;
+    a.n_frames = n_frames;
+    a.g = c->g;
+    for (int b = 0; b < c->g.B; ++b) {
+      a.t0[b] = t0[b];
+      a.pos_off[b] = c->pos_off[b];
+    }
+    for (int j = 0; j < c->g.dt / 2; ++j) a.omega_t[j] = c->om.t[j];
+    return hip_status(scv::launch_qkv_rope(a, static_cast<hipStream_t>(stream)), "qkv_rope_append launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
 int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
                              size_t ws_bytes) {
   try {

@@ -68,6 +68,24 @@ struct RefreshArgs {
   double omega_t[kMaxAxisPairs];
 };
 
+// Fused QKV projection + RoPE + append arguments (by value).
+struct QkvArgs {
+  const void* x;      // [B][Ntok][d_model] layer input (dtype)
+  const void* w;      // [3*H*D][d_model] projection weight (dtype)
+  void* q_out;        // [B][Ntok][H][D] rotated queries (qk_dtype)
+  void* cache_k;
+  void* cache_v;
+  int64_t* stamps;
+  const float2* tab_h;
+  const float2* tab_w;
+  int32_t d_model;
+  int32_t n_frames;
+  Geometry g;
+  int64_t t0[kMaxBatch];
+  int64_t pos_off[kMaxBatch];
+  double omega_t[kMaxAxisPairs];
+};
+
 // Attention kernel arguments (by value).
 struct AttnArgs {
   const void* q;
@@ -106,11 +124,20 @@ inline int attn_rows_per_workgroup(const Geometry& g) {
   return g.dtype == SCV_BF16 ? kAttnRowsBf16 : kAttnRowsF32;
 }
 
+// cos/sin of the fp64 angle pos * omega, rounded to fp32 (round to nearest).
+__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, double omega) {
+  const double th = static_cast<double>(pos) * omega;
+  double s, c;
+  sincos(th, &s, &c);
+  return make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
 hipError_t launch_rope_tables(const Geometry& g, const Omegas& om, const int64_t* t0, int32_t n_frames,
                               float* out_t, float2* out_h, float2* out_w, hipStream_t s);
 hipError_t launch_rope_refresh(const RefreshArgs& a, hipStream_t s);
+hipError_t launch_qkv_rope(const QkvArgs& a, hipStream_t s);
 hipError_t launch_cache_reset(const Geometry& g, void* kv_base, size_t kv_bytes, int64_t* stamps, hipStream_t s);
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t s);

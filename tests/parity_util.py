@@ -41,9 +41,8 @@ def spec_of(w: Workload) -> O.CacheSpec:
     )
 
 
-def oracle_replay(w: Workload):
-    """OracleCache after the same calls as StreamRunner.fill() + append();
-    returns (cache, q_rot fp64)."""
+def oracle_fill(w: Workload):
+    """OracleCache after the same calls as StreamRunner.fill()."""
     oc = O.OracleCache(spec_of(w))
     if w.sink_frames > 0:
         zeros = [0] * w.batch
@@ -51,6 +50,13 @@ def oracle_replay(w: Workload):
     for starts, n in fill_schedule(w):
         k = G.frames_tensor(w, G.TENSOR_K, starts, n)
         oc.kv_append_roll(oc.rope3d_apply(k, starts, n), G.frames_tensor(w, G.TENSOR_V, starts, n), starts, n)
+    return oc
+
+
+def oracle_replay(w: Workload):
+    """OracleCache after the same calls as StreamRunner.fill() + append();
+    returns (cache, q_rot fp64)."""
+    oc = oracle_fill(w)
     nq = w.query_frames
     q_rot = oc.rope3d_append(
         G.frames_tensor(w, G.TENSOR_Q, w.t0, nq),

@@ -258,3 +258,19 @@ def test_auto_splits_respect_workspace_and_t0(lib):
     assert lib.scv_attention_splits(h, t0(20000), 3, 0, big) == s_steady
     assert lib.scv_attention_splits(h, t0(-1), 3, 0, big) == 0
     lib.scv_cache_destroy(h)
+
+
+def test_qkv_validation(lib):
+    cfg, h = make_handle(lib)
+    p = FAKE + (1 << 36)
+    assert lib.scv_qkv_rope_append(h, None, 1536, p, p, t0(5), 3, None) == -1
+    assert lib.scv_qkv_rope_append(h, p, 1536, p, None, t0(5), 3, None) == -1
+    assert lib.scv_qkv_rope_append(h, p + 8, 1536, p, p, t0(5), 3, None) == -4
+    assert lib.scv_qkv_rope_append(h, p, 1000, p, p, t0(5), 3, None) == -2  # not a multiple of 32
+    assert lib.scv_qkv_rope_append(h, p, 0, p, p, t0(5), 3, None) == -2
+    assert lib.scv_qkv_rope_append(h, p, 1536, p, p, t0(-5), 3, None) == -5
+    assert lib.scv_qkv_rope_append(h, p, 1536, p, p, t0(5), 16, None) == -2  # more ring frames than R
+    lib.scv_cache_destroy(h)
+    cfg, h = make_handle(lib, dtype="fp32", head_dim=64, split=(24, 20, 20))
+    assert lib.scv_qkv_rope_append(h, p, 64, p, p, t0(5), 3, None) == -3
+    lib.scv_cache_destroy(h)
