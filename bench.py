@@ -133,6 +133,34 @@ def cpu_baseline(w, target_s=12.0):
     }
 
 
+def time_qkv(r, w, reps=20):
+    """HIP-event time of the QKV projection fused with RoPE and the append
+    (d_model = heads * head_dim, the Wan layers' width), replacing the
+    step's rope3d_append: FLOPs 2 * tokens * d_model * 3*H*d."""
+    import torch
+
+    from streaming_causal_video_amd import datagen as G
+    from streaming_causal_video_amd.runner import to_device
+
+    d_model = w.heads * w.head_dim
+    n = w.query_frames
+    x = to_device(G.hidden_frames(w, d_model, w.t0, n), "bf16")
+    wq = to_device(G.qkv_weight(w, d_model), "bf16")
+    fn = lambda: r.cache.qkv_rope_append(x, wq, r.q_rot, w.t0, n)  # noqa: E731
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / reps
+    flops = 2.0 * w.batch * w.query_rows * d_model * 3 * w.heads * w.head_dim
+    tf = flops / (us * 1e-6) / 1e12
+    return {"us": us, "d_model": d_model, "flops": flops, "tflops": tf, "frac_mfma": tf / PEAK_TFLOPS["bf16"]}
+
+
 def time_refresh_and_sink(r, w, reps=20):
     """HIP-event times of the RoPE refresh (every cached key's time pairs,
     one launch) and of a one-frame sink update, on the launch stream, after
@@ -275,6 +303,8 @@ def main():
     if r.splits > 1:
         out["attn_ms_includes_merge"] = True
     out["next_rows"] = time_refresh_and_sink(r, w)
+    if w.dtype == "bf16":
+        out["next_rows"]["qkv_rope_append"] = time_qkv(r, w)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

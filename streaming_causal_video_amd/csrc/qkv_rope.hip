@@ -10,12 +10,12 @@
 // through HBM between the two.
 //
 // GEMM: C = x W^T with M = tokens of one stream, N = 3*H*D features, K =
-// d_model.  A workgroup computes one head of q, k or v (D features) for 256
-// tokens; 4 waves (one per SIMD) of 64 tokens x D features, fp32
-// accumulators in VGPRs, 32x32x16 bf16 MFMA.  Both operands are K-contiguous
-// in memory (x rows, weight rows) and move global -> LDS with the 16-byte
-// direct loads of gfx950 into a 3-stage ring of 32-deep K slices (24 KB per
-// stage at D = 128, so two workgroups share a CU).  Rows of a slice are 64
+// d_model.  A workgroup computes two feature blocks of D features (two
+// heads of q, k or v) for 256 tokens; 8 waves (two per SIMD) of 64 tokens x
+// D features, fp32 accumulators in VGPRs, 32x32x16 bf16 MFMA.  Both operands
+// are K-contiguous in memory (x rows, weight rows) and move global -> LDS
+// with the 16-byte direct loads of gfx950 into a 4-stage ring of 32-deep K
+// slices (32 KB per stage at D = 128), loaded three slices ahead.  Rows of a slice are 64
 // bytes; the 16-byte chunk c of row r sits at c ^ ((r >> 2) & 3), which puts
 // any 16 consecutive rows of a fragment read on distinct banks.
 // For q and k the MFMA computes C^T (features as rows) so that each lane
@@ -35,8 +35,8 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kQM = 256;       // tokens per workgroup
 constexpr int kQK = 32;        // reduction depth of one LDS stage
-constexpr int kQStages = 3;
-constexpr int kQWaves = 4;     // 64 tokens per wave
+constexpr int kQStages = 4;
+constexpr int kQWaves = 8;     // two groups of 4 waves, one feature block (head) each
 constexpr int kTabFrames = 8;  // time-axis cos/sin of up to 8 frames in LDS
 
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
@@ -55,25 +55,47 @@ __device__ __forceinline__ uint16_t bits16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<T>(x));
 }
 
+// One workgroup: 256 tokens of one stream x two feature blocks of D
+// features (two heads of q, k or v; the blocks may belong to different
+// ones).  Waves 0-3 compute block 0, waves 4-7 block 1, each wave 64 tokens.
 template <typename QT, int D>
-__global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
+__global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   constexpr int XB = kQM * kQK * 2;            // x slice bytes
-  constexpr int WB = D * kQK * 2;              // weight slice bytes
+  constexpr int WB = 2 * D * kQK * 2;          // weight slice bytes (two blocks)
   constexpr int STAGE = XB + WB;
   constexpr int X_DMA = XB / 1024 / kQWaves;   // 1 KB loads per wave per stage
   constexpr int W_DMA = WB / 1024 / kQWaves;
   constexpr int DMA = X_DMA + W_DMA;
   constexpr int DB = D / 32, TB = 2;
-  static_assert(W_DMA >= 1, "tile sizes");
+  static_assert(X_DMA >= 1 && W_DMA >= 1, "tile sizes");
   __shared__ __attribute__((aligned(1024))) char smem[kQStages * STAGE];
   __shared__ float2 tab_t[kTabFrames * kMaxAxisPairs];
 
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3;  // feature block of this wave, token quarter
   const int hl = lane >> 5, l32 = lane & 31;
-  const int mt = blockIdx.x, nb = blockIdx.y, b = blockIdx.z;
-  const int sel = nb / g.H, head = nb - sel * g.H;  // 0: q, 1: k, 2: v
+  // Workgroups go to the 8 XCDs round robin; renumber them so that each
+  // XCD runs a contiguous range of (token tile fastest, feature pair,
+  // stream): its few feature pairs' weights stay in its L2 while the token
+  // tiles stream past.
+  int mt, fpair, b;
+  {
+    const int nx = gridDim.x, ny = gridDim.y, n = nx * ny * gridDim.z;
+    const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const int xcd = id % 8, k = id / 8;
+    const int base = n / 8, extra = n % 8;
+    const int logical = xcd * base + min(xcd, extra) + k;
+    mt = logical % nx;
+    fpair = (logical / nx) % ny;
+    b = logical / (nx * ny);
+  }
+  const int n_blocks = 3 * g.H;
+  const int fb0 = 2 * fpair;
+  const int fb = fb0 + grp;                  // this wave's feature block
+  const bool fb_valid = fb < n_blocks;
+  const int sel = fb / g.H, head = fb - sel * g.H;  // 0: q, 1: k, 2: v
   const int Ntok = a.n_frames * g.P;
   const int m0 = mt * kQM;
   const int Dm = a.d_model;
@@ -81,9 +103,9 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
   const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
 
   // time-axis cos/sin of the frames this tile starts in (fp64 angles)
-  if (sel < 2) {
+  {
     const int nf = min(kTabFrames, a.n_frames - f_lo);
-    for (int i = tid; i < nf * pt; i += 256) {
+    for (int i = tid; i < nf * pt; i += 512) {
       const int fi = i / pt, j = i - fi * pt;
       tab_t[fi * kMaxAxisPairs + j] = rope_cos_sin(a.t0[b] + f_lo + fi - a.pos_off[b], a.omega_t[j]);
     }
@@ -92,7 +114,8 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
   // ---- global -> LDS slices (source offsets are loop invariant) ----
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
   const char* xbase = static_cast<const char*>(a.x) + int64_t(b) * Ntok * Dm * 2;
-  const char* wbase = static_cast<const char*>(a.w) + int64_t(nb) * D * Dm * 2;
+  const char* wbase = static_cast<const char*>(a.w) + int64_t(fb0) * D * Dm * 2;
+  const int w_rows = min(2, n_blocks - fb0) * D;  // weight rows that exist
   uint32_t xo[X_DMA], wo[W_DMA];
 #pragma unroll
   for (int j = 0; j < X_DMA; ++j) {
@@ -103,7 +126,8 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
 #pragma unroll
   for (int j = 0; j < W_DMA; ++j) {
     const int piece = (wave * W_DMA + j) * 64 + lane, r = piece >> 2, cs = piece & 3;
-    wo[j] = uint32_t(r) * uint32_t(Dm * 2) + uint32_t((cs ^ ((r >> 2) & 3)) << 4);
+    const int rr = min(r, w_rows - 1);  // a missing second block repeats the last row (unused)
+    wo[j] = uint32_t(rr) * uint32_t(Dm * 2) + uint32_t((cs ^ ((r >> 2) & 3)) << 4);
   }
   auto issue = [&](int kt, int stg) {
     const uint32_t dst = lds0 + uint32_t(stg * STAGE);
@@ -123,41 +147,68 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xoff[kk][tb] = slice_off(64 * wave + 32 * tb + l32, 2 * kk + hl);
+    for (int tb = 0; tb < TB; ++tb) xoff[kk][tb] = slice_off(64 * wq + 32 * tb + l32, 2 * kk + hl);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) woff[kk][db] = XB + slice_off(32 * db + l32, 2 * kk + hl);
+    for (int db = 0; db < DB; ++db) woff[kk][db] = XB + slice_off(D * grp + 32 * db + l32, 2 * kk + hl);
   }
 
+  // Every wave passes the same barriers; the MFMA operand order (C^T for q
+  // and k, C for v) is per wave.  Fragments of the next 16-deep step are read
+  // while the MFMAs of the current one run, also across the barrier that
+  // publishes the next slice: a trip reads step 1 of slice kt, runs step 0,
+  // waits for slice kt+1, reads its step 0 and runs step 1 of slice kt.
+  struct Frags {
+    bf16x8_t x[TB], w[DB];
+  };
+  auto read = [&](const char* st, int kk, Frags& f) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) f.x[tb] = *reinterpret_cast<const bf16x8_t*>(st + xoff[kk][tb]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) f.w[db] = *reinterpret_cast<const bf16x8_t*>(st + woff[kk][db]);
+  };
   auto gemm = [&](auto trans_tag) {
     constexpr bool kTrans = decltype(trans_tag)::value;  // C^T: features as rows
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          if constexpr (kTrans)
+            acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[db], f.x[tb], acc[db * TB + tb], 0, 0, 0);
+          else
+            acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[tb], f.w[db], acc[db * TB + tb], 0, 0, 0);
+        }
+    };
     const int n_k = Dm / kQK;
-    issue(0, 0);
-    if (n_k > 1) issue(1, 1);
-    for (int kt = 0; kt < n_k; ++kt) {
-      if (kt + 1 < n_k)
+    // wait until slice kt has landed (slices after it may still be loading)
+    auto wait_slice = [&](int kt) {
+      const int ahead = min(n_k - 1 - kt, kQStages - 2);
+      if (ahead >= 2)
+        wait_vm<2 * DMA>();
+      else if (ahead == 1)
         wait_vm<DMA>();
       else
         wait_vm<0>();
-      __syncthreads();  // slice kt landed everywhere; slice kt-1 is done everywhere
-      if (kt + 2 < n_k) issue(kt + 2, (kt + 2) % kQStages);
+    };
+#pragma unroll
+    for (int i = 0; i < kQStages - 1; ++i)
+      if (i < n_k) issue(i, i);
+    wait_slice(0);
+    __syncthreads();
+    if (kQStages - 1 < n_k) issue(kQStages - 1, kQStages - 1);
+    Frags f0, f1;
+    read(smem, 0, f0);
+    for (int kt = 0; kt < n_k; ++kt) {
       const char* st = smem + (kt % kQStages) * STAGE;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t xf[TB], wf[DB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) xf[tb] = *reinterpret_cast<const bf16x8_t*>(st + xoff[kk][tb]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) wf[db] = *reinterpret_cast<const bf16x8_t*>(st + woff[kk][db]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb) {
-            if constexpr (kTrans)
-              acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[db], xf[tb], acc[db * TB + tb], 0, 0, 0);
-            else
-              acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[tb], wf[db], acc[db * TB + tb], 0, 0, 0);
-          }
+      read(st, 1, f1);
+      mma(f0);
+      if (kt + 1 < n_k) {
+        wait_slice(kt + 1);
+        __syncthreads();  // slice kt+1 landed everywhere; slice kt-1... kt's reads are done everywhere
+        if (kt + kQStages < n_k) issue(kt + kQStages, (kt + kQStages) % kQStages);
+        read(smem + ((kt + 1) % kQStages) * STAGE, 0, f0);
       }
+      mma(f1);
     }
   };
 
@@ -169,10 +220,11 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
 
   if (sel < 2) {
     gemm(std::true_type{});
-    // lane: token 64w + 32tb + l32 of the tile; dims 32db + 8e + 4hl + 0..3
+    if (!fb_valid) return;  // after the last barrier
+    // lane: token 64wq + 32tb + l32 of the tile; dims 32db + 8e + 4hl + 0..3
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int t = m0 + 64 * wave + 32 * tb + l32;
+      const int t = m0 + 64 * wq + 32 * tb + l32;
       if (t >= Ntok) continue;
       const int f = t / g.P, p = t - f * g.P;
       const int yy = p / g.grid_w, xx = p - yy * g.grid_w;
@@ -212,7 +264,8 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
     }
   } else {
     gemm(std::false_type{});
-    // lane: feature 32db + l32; tokens 64w + 32tb + 8e + 4hl + 0..3
+    if (!fb_valid) return;
+    // lane: feature 32db + l32; tokens 64wq + 32tb + 8e + 4hl + 0..3
     uint16_t* vt = static_cast<uint16_t*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -221,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tk = m0 + 64 * wave + 32 * tb + 8 * e + 4 * hl;
+          const int tk = m0 + 64 * wq + 32 * tb + 8 * e + 4 * hl;
           if (tk >= Ntok) continue;
           const floatx16_t& c = acc[db * TB + tb];
           const int f = tk / g.P, p = tk - f * g.P;
@@ -241,8 +294,9 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
           }
         }
     }
-    // stamps: the frames whose first token lies in this tile
-    if (head == 0 && tid == 0) {
+    // stamps: the frames whose first token lies in this tile (one writer:
+    // the wave group holding v head 0)
+    if (head == 0 && wq == 0 && lane == 0) {
       for (int f = (m0 + g.P - 1) / g.P; f * g.P < min(m0 + kQM, Ntok); ++f)
         a.stamps[int64_t(b) * g.n_slots + slot_of(f)] = t0 + f;
     }
@@ -252,8 +306,8 @@ __global__ __launch_bounds__(256, 2) void qkv_rope_kernel(QkvArgs a) {
 template <typename QT, int D>
 hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s) {
   const int ntok = a.n_frames * a.g.P;
-  dim3 grid(unsigned((ntok + kQM - 1) / kQM), unsigned(3 * a.g.H), unsigned(a.g.B));
-  hipLaunchKernelGGL((qkv_rope_kernel<QT, D>), grid, dim3(256), 0, s, a);
+  dim3 grid(unsigned((ntok + kQM - 1) / kQM), unsigned((3 * a.g.H + 1) / 2), unsigned(a.g.B));
+  hipLaunchKernelGGL((qkv_rope_kernel<QT, D>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
