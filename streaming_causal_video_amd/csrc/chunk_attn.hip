@@ -575,7 +575,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     // so each runs M(i) while its SIMD partner runs V(i-1), and V(i) while
     // the partner runs M(i+1).  Every wave loads its share of each tile:
     // tile i+2 (into the stage of tile i-2, which both groups finished before
-    // the barrier that starts the wave's trip) as its M(i) starts; tile i+1
+    // the barrier that starts the wave's M(i)) as its V(i) starts; tile i+1
     // is waited for before the barrier that ends the lead waves' V(i), which
     // publishes it.  Every wave passes the same number of barriers.
     bool f0 = true, f1 = true;                              // fully visible?
@@ -597,35 +597,32 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         const bool cur = tq0 < t_end;
         int tq2 = t_end;
         bool f2 = true;
-        auto wait_next = [&]() {
-          if (tq1 < t_end) {
-            if (tq2 < t_end)
-              wait_vm<T::DMA>();
-            else
-              wait_vm<0>();
-          }
-        };
-        if (tq1 < t_end) {
-          tq2 = next_tile(false, &f2);
-          if (tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
-        }
+        if (tq1 < t_end) tq2 = next_tile(false, &f2);
         // M(i)
         const char* st = smem + si * T::STAGE;
         const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
         if (have_prev) pv(stp);
         if (cur) qk(st);
         // each wave's share of tile i+1 has landed before the barrier after
-        // which the first reader (a lead wave in M(i+1)) may start
-        if (!lead) wait_next();
+        // which the first reader (a lead wave in M(i+1)) may start; a
+        // non-lead wave has issued nothing after it
+        if (!lead && tq1 < t_end) wait_vm<0>();
         __syncthreads();
-        // V(i)
+        // V(i): the load of tile i+2 goes out here, in the VALU phase, so
+        // that its issue never holds up the MFMA phase
+        if (tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
         if (cur) {
           if constexpr (kMasked) {
             if (!f0) mask(tq0);
           }
           softmax();
         }
-        if (lead) wait_next();
+        if (lead && tq1 < t_end) {
+          if (tq2 < t_end)
+            wait_vm<T::DMA>();
+          else
+            wait_vm<0>();
+        }
         __syncthreads();
         if (!cur) break;
         have_prev = true;
