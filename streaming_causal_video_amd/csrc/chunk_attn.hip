@@ -601,8 +601,11 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         // M(i)
         const char* st = smem + si * T::STAGE;
         const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
+        // the MFMA phase outranks the partner wave's softmax at issue
+        __builtin_amdgcn_s_setprio(1);
         if (have_prev) pv(stp);
         if (cur) qk(st);
+        __builtin_amdgcn_s_setprio(0);
         // each wave's share of tile i+1 has landed before the barrier after
         // which the first reader (a lead wave in M(i+1)) may start; a
         // non-lead wave has issued nothing after it
