@@ -42,10 +42,6 @@ COMMON = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
-    # keep MFMA accumulators in VGPRs (the softmax reads S and rescales O
-    # with VALU instructions; AGPR accumulators would need copies)
-    "-mllvm",
-    "-amdgpu-mfma-vgpr-form",
     "-I",
     INCLUDE,
     "-I",
@@ -53,8 +49,14 @@ COMMON = [
 ]
 
 
-# Per-source additions (none at present).
-PER_FILE: dict = {}
+# Per-source additions.
+PER_FILE: dict = {
+    # keep MFMA accumulators in VGPRs: the softmax reads S and rescales O with
+    # VALU instructions, which AGPR accumulators would need copies for (the
+    # projection GEMM, whose accumulators only meet VALU code once, in its
+    # epilogue, keeps them in AGPRs)
+    "chunk_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str, hipcc: str) -> str:

@@ -36,7 +36,6 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 constexpr int kQM = 256;       // tokens per workgroup
 constexpr int kQK = 32;        // reduction depth of one LDS stage
 constexpr int kQStages = 4;
-constexpr int kQWaves = 8;     // two groups of 4 waves, one feature block (head) each
 constexpr int kTabFrames = 8;  // time-axis cos/sin of up to 8 frames in LDS
 
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
@@ -57,16 +56,22 @@ __device__ __forceinline__ uint16_t bits16(float x) {
 
 // One workgroup: 256 tokens of one stream x two feature blocks of D
 // features (two heads of q, k or v; the blocks may belong to different
-// ones).  Waves 0-3 compute block 0, waves 4-7 block 1, each wave 64 tokens.
-template <typename QT, int D>
-__global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
+// ones).  Each wave computes 32*TB tokens of one block.  The launches use
+// TB = 2: 8 waves, two per SIMD, so that one wave's MFMAs cover the other's
+// waits (TB = 4 -- 4 waves of 128x128 tiles, half the LDS bytes per MFMA --
+// measured 1.5x slower: a lone wave per SIMD stalls on its own loads).
+template <typename QT, int D, int TB>
+__global__ __launch_bounds__(2 * (kQM / (32 * TB)) * 64, 1) void qkv_rope_kernel(QkvArgs a) {
+  constexpr int kTokGroups = kQM / (32 * TB);   // waves per feature block
+  constexpr int kQWaves = 2 * kTokGroups;
+  constexpr int kThreads = 64 * kQWaves;
   constexpr int XB = kQM * kQK * 2;            // x slice bytes
   constexpr int WB = 2 * D * kQK * 2;          // weight slice bytes (two blocks)
   constexpr int STAGE = XB + WB;
   constexpr int X_DMA = XB / 1024 / kQWaves;   // 1 KB loads per wave per stage
   constexpr int W_DMA = WB / 1024 / kQWaves;
   constexpr int DMA = X_DMA + W_DMA;
-  constexpr int DB = D / 32, TB = 2;
+  constexpr int DB = D / 32;
   static_assert(X_DMA >= 1 && W_DMA >= 1, "tile sizes");
   __shared__ __attribute__((aligned(1024))) char smem[kQStages * STAGE];
   __shared__ float2 tab_t[kTabFrames * kMaxAxisPairs];
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wq = wave & 3;  // feature block of this wave, token quarter
+  const int grp = wave / kTokGroups, wq = wave % kTokGroups;  // feature block, token group
   const int hl = lane >> 5, l32 = lane & 31;
   // Workgroups go to the 8 XCDs round robin; renumber them so that each
   // XCD runs a contiguous range of (token tile fastest, feature pair,
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   // time-axis cos/sin of the frames this tile starts in (fp64 angles)
   {
     const int nf = min(kTabFrames, a.n_frames - f_lo);
-    for (int i = tid; i < nf * pt; i += 512) {
+    for (int i = tid; i < nf * pt; i += kThreads) {
       const int fi = i / pt, j = i - fi * pt;
       tab_t[fi * kMaxAxisPairs + j] = rope_cos_sin(a.t0[b] + f_lo + fi - a.pos_off[b], a.omega_t[j]);
     }
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xoff[kk][tb] = slice_off(64 * wq + 32 * tb + l32, 2 * kk + hl);
+    for (int tb = 0; tb < TB; ++tb) xoff[kk][tb] = slice_off(32 * TB * wq + 32 * tb + l32, 2 * kk + hl);
 #pragma unroll
     for (int db = 0; db < DB; ++db) woff[kk][db] = XB + slice_off(D * grp + 32 * db + l32, 2 * kk + hl);
   }
@@ -221,10 +226,10 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   if (sel < 2) {
     gemm(std::true_type{});
     if (!fb_valid) return;  // after the last barrier
-    // lane: token 64wq + 32tb + l32 of the tile; dims 32db + 8e + 4hl + 0..3
+    // lane: token 32TB*wq + 32tb + l32 of the tile; dims 32db + 8e + 4hl + 0..3
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int t = m0 + 64 * wq + 32 * tb + l32;
+      const int t = m0 + 32 * TB * wq + 32 * tb + l32;
       if (t >= Ntok) continue;
       const int f = t / g.P, p = t - f * g.P;
       const int yy = p / g.grid_w, xx = p - yy * g.grid_w;
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   } else {
     gemm(std::false_type{});
     if (!fb_valid) return;
-    // lane: feature 32db + l32; tokens 64wq + 32tb + 8e + 4hl + 0..3
+    // lane: feature 32db + l32; tokens 32TB*wq + 32tb + 8e + 4hl + 0..3
     uint16_t* vt = static_cast<uint16_t*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tk = m0 + 64 * wq + 32 * tb + 8 * e + 4 * hl;
+          const int tk = m0 + 32 * TB * wq + 32 * tb + 8 * e + 4 * hl;
           if (tk >= Ntok) continue;
           const floatx16_t& c = acc[db * TB + tb];
           const int f = tk / g.P, p = tk - f * g.P;
@@ -303,11 +308,11 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   }
 }
 
-template <typename QT, int D>
+template <typename QT, int D, int TB>
 hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s) {
   const int ntok = a.n_frames * a.g.P;
   dim3 grid(unsigned((ntok + kQM - 1) / kQM), unsigned((3 * a.g.H + 1) / 2), unsigned(a.g.B));
-  hipLaunchKernelGGL((qkv_rope_kernel<QT, D>), grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL((qkv_rope_kernel<QT, D, TB>), grid, dim3(2 * (kQM / (32 * TB)) * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -315,8 +320,8 @@ hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s) {
 
 hipError_t launch_qkv_rope(const QkvArgs& a, hipStream_t s) {
   const bool f16 = a.g.qk_dtype == SCV_FP16;
-  if (a.g.D == 128) return f16 ? launch_qkv_t<_Float16, 128>(a, s) : launch_qkv_t<__bf16, 128>(a, s);
-  return f16 ? launch_qkv_t<_Float16, 64>(a, s) : launch_qkv_t<__bf16, 64>(a, s);
+  if (a.g.D == 128) return f16 ? launch_qkv_t<_Float16, 128, 2>(a, s) : launch_qkv_t<__bf16, 128, 2>(a, s);
+  return f16 ? launch_qkv_t<_Float16, 64, 2>(a, s) : launch_qkv_t<__bf16, 64, 2>(a, s);
 }
 
 }  // namespace scv
