@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md
-    "wan1.3b-480p": {"source": "1a10ead7e5fa067f", "kv_splits": 1, "bytes_per_launch": 272027776},
+    "wan1.3b-480p": {"source": "cc0c8c0db8a97af0", "kv_splits": 1, "bytes_per_launch": 272026521},
 }
 KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
 
