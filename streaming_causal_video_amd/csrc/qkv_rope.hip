@@ -33,9 +33,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kQM = 256;       // tokens per workgroup
 constexpr int kQK = 32;        // reduction depth of one LDS stage
-constexpr int kQStages = 4;
+constexpr int kQTokGroups = 4; // waves per feature block
 constexpr int kTabFrames = 8;  // time-axis cos/sin of up to 8 frames in LDS
 
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
@@ -54,15 +53,19 @@ __device__ __forceinline__ uint16_t bits16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<T>(x));
 }
 
-// One workgroup: 256 tokens of one stream x two feature blocks of D
+// One workgroup: 128*TB tokens of one stream x two feature blocks of D
 // features (two heads of q, k or v; the blocks may belong to different
-// ones).  Each wave computes 32*TB tokens of one block.  The launches use
-// TB = 2: 8 waves, two per SIMD, so that one wave's MFMAs cover the other's
-// waits (TB = 4 -- 4 waves of 128x128 tiles, half the LDS bytes per MFMA --
-// measured 1.5x slower: a lone wave per SIMD stalls on its own loads).
+// ones); 8 waves, two per SIMD, so that one wave's MFMAs cover the other's
+// waits; each wave computes 32*TB tokens of one block.  TB = 3 (384 tokens,
+// a 3-stage ring) gives fewer, larger workgroups than TB = 2 (256 tokens, a
+// 4-stage ring); the host picks the one whose grid fills the chip better.
+// (4 waves of 128x128 tiles -- half the LDS bytes per MFMA -- measured 1.5x
+// slower: a lone wave per SIMD stalls on its own loads.)
 template <typename QT, int D, int TB>
-__global__ __launch_bounds__(2 * (kQM / (32 * TB)) * 64, 1) void qkv_rope_kernel(QkvArgs a) {
-  constexpr int kTokGroups = kQM / (32 * TB);   // waves per feature block
+__global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
+  constexpr int kQM = 32 * TB * kQTokGroups;   // tokens per workgroup
+  constexpr int kQStages = TB >= 3 ? 3 : 4;
+  constexpr int kTokGroups = kQTokGroups;
   constexpr int kQWaves = 2 * kTokGroups;
   constexpr int kThreads = 64 * kQWaves;
   constexpr int XB = kQM * kQK * 2;            // x slice bytes
@@ -198,6 +201,23 @@ __global__ __launch_bounds__(2 * (kQM / (32 * TB)) * 64, 1) void qkv_rope_kernel
 #pragma unroll
     for (int i = 0; i < kQStages - 1; ++i)
       if (i < n_k) issue(i, i);
+    if constexpr (TB >= 3) {
+      // 96-token waves: no registers for a second fragment set; the SIMD's
+      // other wave covers the fragment waits
+      for (int kt = 0; kt < n_k; ++kt) {
+        wait_slice(kt);
+        __syncthreads();  // slice kt landed everywhere; slice kt-1 is done everywhere
+        if (kt + kQStages - 1 < n_k) issue(kt + kQStages - 1, (kt + kQStages - 1) % kQStages);
+        const char* st = smem + (kt % kQStages) * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          Frags f;
+          read(st, kk, f);
+          mma(f);
+        }
+      }
+      return;
+    }
     wait_slice(0);
     __syncthreads();
     if (kQStages - 1 < n_k) issue(kQStages - 1, kQStages - 1);
@@ -311,17 +331,23 @@ __global__ __launch_bounds__(2 * (kQM / (32 * TB)) * 64, 1) void qkv_rope_kernel
 template <typename QT, int D, int TB>
 hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s) {
   const int ntok = a.n_frames * a.g.P;
-  dim3 grid(unsigned((ntok + kQM - 1) / kQM), unsigned((3 * a.g.H + 1) / 2), unsigned(a.g.B));
-  hipLaunchKernelGGL((qkv_rope_kernel<QT, D, TB>), grid, dim3(2 * (kQM / (32 * TB)) * 64), 0, s, a);
+  const int qm = 32 * TB * kQTokGroups;
+  dim3 grid(unsigned((ntok + qm - 1) / qm), unsigned((3 * a.g.H + 1) / 2), unsigned(a.g.B));
+  hipLaunchKernelGGL((qkv_rope_kernel<QT, D, TB>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename QT, int D>
+hipError_t launch_qkv_d(const QkvArgs& a, hipStream_t s) {
+  return a.token_tile == 384 ? launch_qkv_t<QT, D, 3>(a, s) : launch_qkv_t<QT, D, 2>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_qkv_rope(const QkvArgs& a, hipStream_t s) {
   const bool f16 = a.g.qk_dtype == SCV_FP16;
-  if (a.g.D == 128) return f16 ? launch_qkv_t<_Float16, 128, 2>(a, s) : launch_qkv_t<__bf16, 128, 2>(a, s);
-  return f16 ? launch_qkv_t<_Float16, 64, 2>(a, s) : launch_qkv_t<__bf16, 64, 2>(a, s);
+  if (a.g.D == 128) return f16 ? launch_qkv_d<_Float16, 128>(a, s) : launch_qkv_d<__bf16, 128>(a, s);
+  return f16 ? launch_qkv_d<_Float16, 64>(a, s) : launch_qkv_d<__bf16, 64>(a, s);
 }
 
 }  // namespace scv

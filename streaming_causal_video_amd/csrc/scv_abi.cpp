@@ -562,6 +562,15 @@ scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, con
     a.d_model = d_model;
     a.n_frames = n_frames;
     a.g = c->g;
+    {
+      // token tile: rounds of workgroups over the compute units times the
+      // work of one workgroup (proportional to its token count)
+      const int64_t ntok = int64_t(n_frames) * c->g.P;
+      const int64_t pairs = (3 * int64_t(c->g.H) + 1) / 2 * c->g.B;
+      const int cus = device_cu_count();
+      auto cost = [&](int64_t tile) { return ((ntok + tile - 1) / tile * pairs + cus - 1) / cus * tile; };
+      a.token_tile = cost(384) < cost(256) ? 384 : 256;
+    }
     for (int b = 0; b < c->g.B; ++b) {
       a.t0[b] = t0[b];
       a.pos_off[b] = c->pos_off[b];

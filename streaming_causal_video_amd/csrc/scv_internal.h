@@ -80,6 +80,7 @@ struct QkvArgs {
   const float2* tab_w;
   int32_t d_model;
   int32_t n_frames;
+  int32_t token_tile;  // tokens per workgroup: 256 or 384
   Geometry g;
   int64_t t0[kMaxBatch];
   int64_t pos_off[kMaxBatch];
