@@ -9,27 +9,27 @@
 // "Accelerating Video Generation Inference with Sequential-Parallel 3D
 // Positional Encoding Using a Global Time Index" (sections 1 and 2).
 //
-// Kernel design (MI355X / CDNA4, wave64):
-//  * Workgroup = 4 waves = 128 query rows of one (stream, head[, key split]);
-//    each wave owns 32 query rows for the whole key loop.
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
-//    wave's Q held in VGPRs).  In the accumulator each lane then holds one
-//    query column and 16 of every 32 keys, so the row max / row sum need a
-//    single exchange with lane ^ 32, and P^T (rounded to bf16) is directly
-//    the B operand of O^T += V^T P^T -- no LDS round trip for P.
-//  * V is stored transposed in the cache ([d][row]); staging permutes keys
-//    inside each 16-key group as 0-3,8-11 | 4-7,12-15 so that the V^T A
-//    operand of each lane is one 16-byte LDS read matching P^T's key order.
-//  * K and V^T tiles (64 keys) are double-buffered in LDS with XOR chunk
-//    swizzles; global loads for tile i+1 are issued before the MFMAs of tile
-//    i and written to LDS after them, one barrier per tile.
+// Kernels (MI355X / CDNA4, wave64):
+//  * chunk_attn_bf16_kernel (bf16 / fp16 operands, fp32 accumulation):
+//    8 waves = 256 query rows of one query chunk of one (stream, head[, key
+//    split]), 32 rows per wave, two waves per SIMD in ping-pong (one in its
+//    MFMA phase while the other runs its softmax); 64-key tiles move global
+//    -> LDS by direct 16-byte loads into a 4-stage ring.  Details above the
+//    kernel.
+//  * chunk_attn_f32_kernel (fp32 end to end): 4 waves = 128 query rows,
+//    v_mfma_f32_32x32x2_f32, double-buffered LDS tiles staged through VGPRs.
+//  * attn_merge_kernel: combines the normalised fp32 partials of key splits
+//    (lse-weighted).
+// Shared by both attention kernels:
+//  * S^T = K Q^T on MFMA (A = K rows from LDS, B = the wave's Q in VGPRs),
+//    so each lane holds one query column and 16 of every 32 keys: the row
+//    max / row sum need one exchange with lane ^ 32, and P^T is directly the
+//    B operand of O^T += V^T P^T -- no LDS round trip for P.
+//  * V is stored transposed in the cache ([d][row]).
 //  * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
-//  * Frame visibility is evaluated once per workgroup from the slot stamps;
-//    tiles no query of the workgroup may see are skipped, fully visible
-//    tiles run unmasked, others are masked per key.
-//  * Optional key splits write normalised fp32 partials + lse, combined by
-//    attn_merge (lse-weighted).
-// An fp32 instantiation (v_mfma_f32_32x32x2_f32) follows the same structure.
+//  * Query tiles never straddle query chunks; each workgroup derives the
+//    slots its chunk may see from the stamps once, skips invisible tiles and
+//    masks the hidden keys of partly visible ones.
 #include <type_traits>
 
 #include "scv_internal.h"
