@@ -11,13 +11,14 @@
 //
 // GEMM: C = x W^T with M = tokens of one stream, N = 3*H*D features, K =
 // d_model.  A workgroup computes two feature blocks of D features (two
-// heads of q, k or v) for 256 tokens; 8 waves (two per SIMD) of 64 tokens x
-// D features, fp32 accumulators in VGPRs, 32x32x16 bf16 MFMA.  Both operands
-// are K-contiguous in memory (x rows, weight rows) and move global -> LDS
-// with the 16-byte direct loads of gfx950 into a 4-stage ring of 32-deep K
-// slices (32 KB per stage at D = 128), loaded three slices ahead.  Rows of a slice are 64
-// bytes; the 16-byte chunk c of row r sits at c ^ ((r >> 2) & 3), which puts
-// any 16 consecutive rows of a fragment read on distinct banks.
+// heads of q, k or v) for 256 or 384 tokens; 8 waves (two per SIMD) of 64
+// or 96 tokens x D features, fp32 accumulators, 32x32x16 bf16 MFMA.  Both
+// operands are K-contiguous in memory (x rows, weight rows) and move global
+// -> LDS with the 16-byte direct loads of gfx950 into a ring of 32-deep K
+// slices (4 stages of 32 KB, or 3 of 40 KB, at D = 128), loaded up to three
+// slices ahead.  Rows of a slice are 64 bytes; the 16-byte chunk c of row r
+// sits at c ^ ((r >> 2) & 3), which puts any 16 consecutive rows of a
+// fragment read on distinct banks.
 // For q and k the MFMA computes C^T (features as rows) so that each lane
 // holds the dim pairs (2j, 2j+1) of one token, which RoPE rotates in
 // registers; for v it computes C (tokens as rows) so that each lane holds 4
