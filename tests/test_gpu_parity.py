@@ -169,6 +169,19 @@ def test_split_kv_small(splits, gpu_lib):
     assert d <= 2.0 ** -7
 
 
+@pytest.mark.parametrize("splits", [2, 5])
+def test_split_kv_multichunk(splits, gpu_lib):
+    """Key splits over several query chunks, one of them near the stream
+    start (the chunks see different numbers of keys)."""
+    w = small("split-multichunk", batch=2, grid_h=4, grid_w=8, window_frames=3, max_query_chunks=3, t0=(2, 40),
+              seed=140)
+    say(f"case split {w.name} splits={splits}")
+    r = run_gpu(w, kv_splits=splits)
+    assert r.splits == splits
+    oc, q_rot = oracle_replay(w)
+    check_attention(r, oc, q_rot, w)
+
+
 def test_split_kv_720p(gpu_lib):
     w = W.WAN13B_720P
     say(f"case split {w.name} splits=4")

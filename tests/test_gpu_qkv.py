@@ -36,6 +36,7 @@ CASES = [
     small("qkv-qkfp16", 160, grid_h=6, grid_w=8, t0=(3000,), qk_dtype="fp16", seed=305),
     small("qkv-long-tiles", 192, heads=2, grid_h=20, grid_w=26, chunk_frames=2, window_frames=6, t0=(50,), seed=306),
     small("qkv-t0-0", 64, batch=2, t0=(0, 1), seed=307),
+    small("qkv-multichunk", 96, grid_h=5, grid_w=12, window_frames=3, max_query_chunks=3, t0=(20,), seed=308),
 ]
 
 
