@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md
-    "wan1.3b-480p": {"source": "cc0c8c0db8a97af0", "kv_splits": 1, "bytes_per_launch": 272026521},
+    "wan1.3b-480p": {"source": "750e12a34d5ab060", "kv_splits": 1, "bytes_per_launch": 272026419},
 }
 KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
 
@@ -133,6 +133,74 @@ def cpu_baseline(w, target_s=12.0):
     }
 
 
+def cold_step_ms(r, reps=5, flush_bytes=512 << 20):
+    """Mean append and attention times with L2 and the 256 MB Infinity Cache
+    flushed before each step by a 512 MB device write (outside the events)."""
+    import torch
+
+    junk = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    app = att = 0.0
+    for _ in range(reps):
+        junk.fill_(1)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        r.append()
+        e[1].record()
+        r.attend()
+        e[2].record()
+        torch.cuda.synchronize()
+        app += e[0].elapsed_time(e[1])
+        att += e[1].elapsed_time(e[2])
+    del junk
+    return {"append_ms": app / reps, "attn_ms": att / reps, "reps": reps, "flush_bytes": flush_bytes}
+
+
+def ablations(w):
+    """Before/after timings of design choices that can be switched from the
+    API: fused rope3d_append vs rope3d_apply + kv_append_roll, and key
+    splits.  One JSON line."""
+    import torch
+
+    from streaming_causal_video_amd.runner import StreamRunner
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+    out = {"workload": w.name}
+    r = StreamRunner(w, kv_splits=1)
+    r.fill()
+    r.step()
+    torch.cuda.synchronize()
+    q_tmp, k_tmp = r.q.clone(), r.k.clone()
+
+    def unfused():
+        q_tmp.copy_(r.q)
+        k_tmp.copy_(r.k)
+        r.cache.rope3d_apply(q_tmp, k_tmp, w.t0, r.n_frames)
+        r.cache.kv_append_roll(k_tmp.view(r.cache.qk_dtype), r.v, w.t0, r.n_frames)
+
+    def copies():
+        q_tmp.copy_(r.q)
+        k_tmp.copy_(r.k)
+
+    out["append_fused_ms"] = timed(r.append)
+    out["append_unfused_ms"] = timed(unfused) - timed(copies)
+    for sp in (1, 2, 4, 8):
+        rs = StreamRunner(w, kv_splits=sp)
+        rs.fill()
+        rs.step()
+        out[f"attn_ms_splits_{sp}"] = timed(rs.attend)
+    print(json.dumps(out), flush=True)
+
+
 def time_qkv(r, w, reps=20):
     """HIP-event time of the QKV projection fused with RoPE and the append
     (d_model = heads * head_dim, the Wan layers' width), replacing the
@@ -205,6 +273,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--ablations", action="store_true",
+                    help="only print before/after timings of API-switchable design choices")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -223,6 +293,9 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     log(f"bench: {w.name}: {w.description}")
+    if args.ablations:
+        ablations(w)
+        return
     r = StreamRunner(w, kv_splits=args.splits)
     r.fill()
     r.step()
@@ -251,6 +324,9 @@ def main():
     ms_per_step = total_ms / K
     append_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    attn_each = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    pct = lambda q: attn_each[min(K - 1, int(q * (K - 1) + 0.5))]  # noqa: E731
+    cold = cold_step_ms(r)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
     frames_per_s = w.batch * w.query_frames / (ms_per_step * 1e-3)
@@ -287,7 +363,9 @@ def main():
         "pct_bf16_peak": 100.0 * step_tflops / peak,
         "latent_frames_per_s": frames_per_s,
         "attn_ms": attn_ms,
+        "attn_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "append_ms": append_ms,
+        "cold": cold,
         "attn_kernel_tflops": attn_tflops,
         "append_gbs": append_bytes / (append_ms * 1e-3) / 1e9,
         "wall_s_timed": wall,
