@@ -332,7 +332,10 @@ class Cache:
             if tuple(lse.shape) != want or lse.dtype != torch.float32 or not lse.is_contiguous():
                 raise ValueError(f"lse: need contiguous float32 {want}")
         if ws is None:
-            ws = self.make_workspace(n_frames, kv_splits)  # None when no split is needed
+            # the split count this request gets (from its t0), then exactly
+            # its workspace (None when it runs unsplit)
+            kv_splits = self.attention_splits(n_frames, kv_splits, t0=t0)
+            ws = self.make_workspace(n_frames, kv_splits)
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(
             self.lib.scv_chunk_attention(self.handle, _ptr(q_rot), _t0_array(t0, self.cfg.batch), n_frames, _ptr(o),
