@@ -380,9 +380,9 @@ def main():
     }
     if r.splits > 1:
         out["attn_ms_includes_merge"] = True
-    out["next_rows"] = time_refresh_and_sink(r, w)
-    if w.dtype == "bf16":
-        out["next_rows"]["qkv_rope_append"] = time_qkv(r, w)
+    # the projection first: the refreshes move time positions below t0
+    out["next_rows"] = {"qkv_rope_append": time_qkv(r, w)} if w.dtype == "bf16" else {}
+    out["next_rows"].update(time_refresh_and_sink(r, w))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -196,13 +196,13 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
 }
 
 // Workgroups are handed to the 8 XCDs of the chip round robin by linear
-// index, each XCD with its own L2.  The work items -- (query chunk fastest,
-// then stream/split, then query tile, then head) -- are renumbered so that
+// index, each XCD with its own L2.  The work items -- ((chunk, stream) class
+// fastest, then split, then query tile, then head) -- are renumbered so that
 // every XCD runs a contiguous range of them: the query tiles of one head
 // then share that head's K/V in one L2 instead of each XCD fetching it from
-// HBM, and every XCD gets the same mix of chunks and streams (which differ in
-// length near a stream's start).  Inside its range an XCD takes later chunks
-// first: a later chunk sees at least as many keys, so the longest
+// HBM, and every XCD gets the same mix of classes (chunks and streams differ
+// in length near a stream's start).  Inside its range an XCD starts the
+// classes in the order the host ranks them (longest first), so the longest
 // workgroups start first.
 constexpr int kXcds = 8;
 struct WorkItem {
@@ -219,29 +219,36 @@ __device__ __forceinline__ WorkItem attn_work_item(const AttnArgs& a) {
   const int lo = xcd * base + min(xcd, extra);
   const int cnt = base + (xcd < extra ? 1 : 0);
   const int nch = a.n_qtiles / a.qtiles_per_chunk;
-  // k-th item of the range in descending chunk order
-  int p = k;
-  {
-    int before = 0;
-    for (int c = nch - 1; c >= 0; --c) {
-      const int r = ((c - lo) % nch + nch) % nch;  // first position of chunk c in the range
-      const int m = r < cnt ? (cnt - r + nch - 1) / nch : 0;
-      if (k < before + m) {
-        p = r + nch * (k - before);
-        break;
-      }
-      before += m;
-    }
+  const int ncls = nch * a.g.B;
+  // In [lo, lo + cnt) class position cp sits at positions p = (cp - r0) mod
+  // ncls + ncls*i; classes whose first position lies below `rem` hold one
+  // more item.  items_before(cp) counts the items of the classes before cp.
+  const int q = cnt / ncls, rem = cnt - q * ncls, r0 = lo % ncls;
+  auto items_before = [&](int cp) {
+    const int in_a = max(0, min(cp, min(r0 + rem, ncls)) - r0);  // [r0, r0 + rem) below cp
+    const int in_b = max(0, min(cp, r0 + rem - ncls));           // its wrapped part [0, r0 + rem - ncls)
+    return cp * q + in_a + in_b;
+  };
+  // the class of the k-th item: the last class position cp with items_before(cp) <= k
+  int c_lo = 0, c_hi = ncls - 1;
+  while (c_lo < c_hi) {
+    const int mid = (c_lo + c_hi + 1) >> 1;
+    if (items_before(mid) <= k)
+      c_lo = mid;
+    else
+      c_hi = mid - 1;
   }
-  const int logical = lo + p;
-  const int nz = gridDim.z;
-  const int chunk = logical % nch;
-  const int rest = logical / nch;
-  const int rest2 = rest / nz;
+  const int cp = c_lo;
+  const int p = (cp - r0 + ncls) % ncls + ncls * (k - items_before(cp));
+  const int rest = (lo + p) / ncls;
+  const int split = rest % a.splits;
+  const int rest2 = rest / a.splits;
+  const int cls = a.cls_order[cp];
+  const int chunk = cls % nch, b = cls / nch;
   WorkItem w;
-  w.bz = rest % nz;
   w.qtile = chunk * a.qtiles_per_chunk + rest2 % a.qtiles_per_chunk;
   w.head = rest2 / a.qtiles_per_chunk;
+  w.bz = b * a.splits + split;
   return w;
 }
 

@@ -1,6 +1,7 @@
 // C ABI of the streaming chunk-attention library: argument validation, the
 // cache layout, per-cache constants and kernel launches.  Every entry point
 // validates before enqueueing anything and never lets an exception escape.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -642,6 +643,19 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
       a.n_qtiles = ((n_frames + c->g.C - 1) / c->g.C) * a.qtiles_per_chunk;
     }
     a.splits = splits;
+    {
+      // work classes (chunk, stream), longest first: the keys each chunk can
+      // see once its history is in the cache (ties keep their natural order)
+      const int nch = (n_frames + c->g.C - 1) / c->g.C;
+      const int ncls = nch * c->g.B;
+      int64_t len[scv::kMaxBatch * scv::kMaxQueryChunks];
+      for (int b = 0; b < c->g.B; ++b)
+        for (int ch = 0; ch < nch; ++ch) {
+          a.cls_order[ch + nch * b] = int16_t(ch + nch * b);
+          len[ch + nch * b] = seen_frames(c, t0[b] + int64_t(ch) * c->g.C);
+        }
+      std::stable_sort(a.cls_order, a.cls_order + ncls, [&](int16_t x, int16_t y) { return len[x] > len[y]; });
+    }
     a.tiles_total = int32_t(c->g.rows_pad / scv::kKeyTile);
     a.tiles_per_split = (a.tiles_total + splits - 1) / splits;
     a.scale_ln = float(1.0 / std::sqrt(double(c->g.D)));

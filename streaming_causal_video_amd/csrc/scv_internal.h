@@ -109,6 +109,9 @@ struct AttnArgs {
   float scale_ln;         // 1 / sqrt(D)
   Geometry g;
   int64_t t0[kMaxBatch];
+  // (chunk, stream) work classes, class id = chunk + n_chunks * stream, in
+  // the order workgroups should start (longest first)
+  int16_t cls_order[kMaxBatch * kMaxQueryChunks];
 };
 
 struct MergeArgs {
