@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md
-    "wan1.3b-480p": {"source": "750e12a34d5ab060", "kv_splits": 1, "bytes_per_launch": 272026419},
+    "wan1.3b-480p": {"source": "ffce9c5abd86c406", "kv_splits": 1, "bytes_per_launch": 272029901},
 }
 KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
 
