@@ -193,11 +193,11 @@ def ablations(w):
 
     out["append_fused_ms"] = timed(r.append)
     out["append_unfused_ms"] = timed(unfused) - timed(copies)
-    for sp in (1, 2, 4, 8):
+    for sp in (-1, 1, 2, 4, 8):
         rs = StreamRunner(w, kv_splits=sp)
         rs.fill()
         rs.step()
-        out[f"attn_ms_splits_{sp}"] = timed(rs.attend)
+        out["attn_ms_balanced" if sp < 0 else f"attn_ms_splits_{sp}"] = timed(rs.attend)
     print(json.dumps(out), flush=True)
 
 
@@ -378,7 +378,9 @@ def main():
             "traffic": traffic,
         },
     }
-    if r.splits > 1:
+    if r.splits != 1:
+        # key splits or the balanced schedule: the merge kernel is part of
+        # the attention step (and of the events around it)
         out["attn_ms_includes_merge"] = True
     # the projection first: the refreshes move time positions below t0
     out["next_rows"] = {"qkv_rope_append": time_qkv(r, w)} if w.dtype == "bf16" else {}

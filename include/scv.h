@@ -217,21 +217,39 @@ scv_status scv_time_offsets(const scv_cache* c, int64_t* out);
 scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int64_t* first_frame, int32_t n_frames,
                            void* stream);
 
-/* Number of key splits chunk_attention will use for this request.
- * kv_splits > 0 asks for that many (capped at 64 and at the number of 64-key
- * tiles).  kv_splits = 0 lets a makespan model choose from the device's
- * compute-unit count: with t0 (HOST int64[batch], nullable) it counts the
- * keys each stream's chunks can see; with t0 = NULL it assumes every chunk
- * sees sink + window + chunk (the steady state).  Only split counts whose
- * workspace fits ws_bytes are considered (SIZE_MAX: no limit). */
+/* Schedule chunk_attention will use for this request: a key split count
+ * >= 1 (grid schedule: one workgroup per query tile, head and split), or
+ * SCV_SCHEDULE_BALANCED = -1 (bf16 only: the work, counted in query-tile x
+ * visited-key-tile units, is cut into equal ranges, a multiple of the
+ * compute-unit count of them, each range at most as long as the shortest
+ * query tile's key walk; a query tile cut by range boundaries leaves fp32
+ * partials that a merge kernel combines -- this keeps every compute unit
+ * busy when the query tiles do not fill whole rounds of the chip).
+ * kv_splits > 0 asks for that many splits (capped at 64 and at the number
+ * of 64-key tiles); kv_splits = -1 asks for the balanced schedule (the fp32
+ * path, and tiles too short for it, fall back to one split).  kv_splits = 0
+ * lets a makespan model choose among both from the device's compute-unit
+ * count: with t0 (HOST int64[batch], nullable) it counts the key tiles each
+ * stream's chunks visit; with t0 = NULL it assumes every chunk sees sink +
+ * window + chunk (the steady state).  Only schedules whose workspace fits
+ * ws_bytes are considered (SIZE_MAX: no limit).  Returns 0 on invalid
+ * arguments. */
+#define SCV_SCHEDULE_BALANCED (-1)
 int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
                              size_t ws_bytes);
 
 /* Workspace bytes chunk_attention needs for this request with
- * kv_splits > 0, or the most the steady-state choice of kv_splits = 0 needs
- * (0 when it runs without splits).  With kv_splits = 0, chunk_attention
- * picks among the split counts this workspace (and t0) allows. */
+ * kv_splits > 0 or -1 (steady-state key counts), or the most the
+ * steady-state choice of kv_splits = 0 needs (0 when it runs without
+ * splits).  With kv_splits = 0, chunk_attention picks among the schedules
+ * this workspace (and t0) allows. */
 size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits);
+
+/* Workspace bytes of the schedule scv_attention_splits(c, t0, n_frames,
+ * kv_splits, SIZE_MAX) selects, for these t0 (HOST int64[batch]); 0 on
+ * invalid arguments or when the schedule needs none. */
+size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* t0, int32_t n_frames,
+                                             int32_t kv_splits);
 
 /* chunk_attention(q, cache) -> o.  Block-causal attention of the rotated
  * queries q_rot (qk_dtype) of frames t0[b] .. t0[b]+n_frames-1
@@ -239,10 +257,13 @@ size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32
  * the normalised output in the cache dtype, lse (nullable) the natural-log
  * softmax normaliser.  QK^T and PV run on MFMA with fp32 accumulation
  * (qk_dtype operands for QK^T; dtype operands for PV), softmax in fp32; P is
- * rounded to the dtype before PV.  With more
- * than one split each split writes normalised fp32 partials into ws and a
- * merge kernel combines them (lse-weighted).  kv_splits = 0 chooses as
- * scv_attention_splits(c, t0, n_frames, 0, ws ? ws_bytes : 0) does. */
+ * rounded to the dtype before PV.  With more than one split, or the
+ * balanced schedule, the pieces of a query tile write normalised fp32
+ * partials into ws (256-byte aligned) and a merge kernel combines them
+ * (lse-weighted).  kv_splits (-1, 0 or a split count) chooses as
+ * scv_attention_splits(c, t0, n_frames, kv_splits, ws ? ws_bytes : 0)
+ * does; a forced schedule whose workspace exceeds ws_bytes fails with
+ * SCV_E_WORKSPACE. */
 scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
                                float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream);
 

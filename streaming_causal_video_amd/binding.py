@@ -88,6 +88,7 @@ _SIGNATURES = {
     "scv_sink_update": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
     "scv_attention_splits": (ctypes.c_int32, [_VP, _I64P, ctypes.c_int32, ctypes.c_int32, ctypes.c_size_t]),
     "scv_attention_workspace_bytes": (ctypes.c_size_t, [_VP, ctypes.c_int32, ctypes.c_int32]),
+    "scv_attention_request_workspace_bytes": (ctypes.c_size_t, [_VP, _I64P, ctypes.c_int32, ctypes.c_int32]),
     "scv_chunk_attention": (
         ctypes.c_int,
         [_VP, _VP, _I64P, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _VP, ctypes.c_size_t, _VP],
@@ -306,9 +307,12 @@ class Cache:
             "scv_sink_update",
         )
 
+    SCHEDULE_BALANCED = -1
+
     def attention_splits(self, n_frames, kv_splits=0, t0=None, ws_bytes=None) -> int:
-        """Splits chunk_attention uses (t0: the request's start frames or None
-        for the steady-state estimate; ws_bytes: the workspace it will get)."""
+        """Schedule chunk_attention uses: a split count, or -1 for the
+        balanced schedule (t0: the request's start frames or None for the
+        steady-state estimate; ws_bytes: the workspace it will get)."""
         t = None if t0 is None else _t0_array(t0, self.cfg.batch)
         lim = (1 << 64) - 1 if ws_bytes is None else int(ws_bytes)
         return int(self.lib.scv_attention_splits(self.handle, t, n_frames, kv_splits, lim))
@@ -316,10 +320,16 @@ class Cache:
     def workspace_bytes(self, n_frames, kv_splits=0) -> int:
         return int(self.lib.scv_attention_workspace_bytes(self.handle, n_frames, kv_splits))
 
-    def make_workspace(self, n_frames, kv_splits=0):
+    def request_workspace_bytes(self, t0, n_frames, kv_splits=0) -> int:
+        """Workspace of the schedule this request (its t0) selects."""
+        return int(self.lib.scv_attention_request_workspace_bytes(self.handle, _t0_array(t0, self.cfg.batch),
+                                                                  n_frames, kv_splits))
+
+    def make_workspace(self, n_frames, kv_splits=0, t0=None):
         import torch
 
-        n = self.workspace_bytes(n_frames, kv_splits)
+        n = self.workspace_bytes(n_frames, kv_splits) if t0 is None else \
+            self.request_workspace_bytes(t0, n_frames, kv_splits)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.buffer.device) if n else None
 
     def chunk_attention(self, q_rot, t0, n_frames, o, lse=None, kv_splits=0, ws=None, stream=None):
@@ -332,10 +342,10 @@ class Cache:
             if tuple(lse.shape) != want or lse.dtype != torch.float32 or not lse.is_contiguous():
                 raise ValueError(f"lse: need contiguous float32 {want}")
         if ws is None:
-            # the split count this request gets (from its t0), then exactly
-            # its workspace (None when it runs unsplit)
+            # the schedule this request gets (from its t0), then exactly its
+            # workspace (None when it runs unsplit)
             kv_splits = self.attention_splits(n_frames, kv_splits, t0=t0)
-            ws = self.make_workspace(n_frames, kv_splits)
+            ws = self.make_workspace(n_frames, kv_splits, t0=t0)
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(
             self.lib.scv_chunk_attention(self.handle, _ptr(q_rot), _t0_array(t0, self.cfg.batch), n_frames, _ptr(o),

@@ -30,6 +30,8 @@
 //  * Query tiles never straddle query chunks; each workgroup derives the
 //    slots its chunk may see from the stamps once, skips invisible tiles and
 //    masks the hidden keys of partly visible ones.
+#include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "scv_internal.h"
@@ -336,7 +338,121 @@ struct RunWalk {
     *full = exact ? (t >= ff && t <= fu) : tile_full(g, slots, t);
     return t;
   }
+  // Moves n visits ahead (whole runs at a time), so that the current tile
+  // is the one next() would return after n more calls; valid turns false
+  // when fewer than n visits remain.
+  __device__ __forceinline__ void skip(const Geometry& g, uint64_t slots, int n) {
+    while (valid && n > 0) {
+      const int step = min(n, last - t);
+      t += step;
+      n -= step;
+      if (n == 0) break;
+      valid = open(g, slots, s_next, t + 1);  // the next visit opens the next run
+      --n;
+    }
+  }
 };
+
+// ---------------------------------------------------------------------------
+// Balanced schedule: the work of a launch, counted in units of one query
+// tile against one visited key tile, is cut into lean_ctas equal ranges, one
+// per workgroup, so that every compute unit runs the same number of tile
+// steps whatever the number of query tiles per head (a launch of 228 query
+// tiles on 256 compute units otherwise leaves 28 of them idle).  Items are
+// laid end to end stream-major, then head, query chunk and query tile.
+// ---------------------------------------------------------------------------
+struct LeanItem {
+  int b, head, chunk, tile;  // tile: query tile inside its chunk
+  int64_t start;             // first unit of the item
+  int units;
+};
+
+template <int ROWS>
+__device__ __forceinline__ int chunk_qtiles(const AttnArgs& a, int ch) {
+  return (min(a.rows_per_chunk, a.Nq - ch * a.rows_per_chunk) + ROWS - 1) / ROWS;
+}
+
+// The item holding unit u (0 <= u < lean_units).
+template <int ROWS>
+__device__ __forceinline__ LeanItem lean_item_at(const AttnArgs& a, int64_t u) {
+  const int nch = a.n_qtiles / a.qtiles_per_chunk;
+  LeanItem it{};
+  int64_t base = 0;
+  for (int b = 0; b < a.g.B; ++b) {
+    int64_t per_head = 0;
+    for (int ch = 0; ch < nch; ++ch) per_head += int64_t(chunk_qtiles<ROWS>(a, ch)) * a.cls_units[ch + nch * b];
+    if (u < base + per_head * a.g.H || b == a.g.B - 1) {
+      const int h = int((u - base) / per_head);
+      base += int64_t(h) * per_head;
+      it.b = b;
+      it.head = h;
+      for (int ch = 0; ch < nch; ++ch) {
+        const int un = a.cls_units[ch + nch * b];
+        const int64_t span = int64_t(chunk_qtiles<ROWS>(a, ch)) * un;
+        if (u < base + span || ch == nch - 1) {
+          it.chunk = ch;
+          it.tile = int((u - base) / un);
+          it.start = base + int64_t(it.tile) * un;
+          it.units = un;
+          return it;
+        }
+        base += span;
+      }
+    }
+    base += per_head * a.g.H;
+  }
+  return it;
+}
+
+// The idx-th item (0 <= idx < B * H * query tiles per head).
+template <int ROWS>
+__device__ __forceinline__ LeanItem lean_item_by_index(const AttnArgs& a, int idx) {
+  const int nch = a.n_qtiles / a.qtiles_per_chunk;
+  int per_head_items = 0;
+  for (int ch = 0; ch < nch; ++ch) per_head_items += chunk_qtiles<ROWS>(a, ch);
+  LeanItem it{};
+  it.b = idx / (per_head_items * a.g.H);
+  it.head = (idx / per_head_items) % a.g.H;
+  int r = idx % per_head_items;
+  int64_t base = 0;
+  for (int b = 0; b < it.b; ++b) {
+    int64_t per_head = 0;
+    for (int ch = 0; ch < nch; ++ch) per_head += int64_t(chunk_qtiles<ROWS>(a, ch)) * a.cls_units[ch + nch * b];
+    base += per_head * a.g.H;
+  }
+  int64_t per_head = 0;
+  for (int ch = 0; ch < nch; ++ch) per_head += int64_t(chunk_qtiles<ROWS>(a, ch)) * a.cls_units[ch + nch * it.b];
+  base += per_head * it.head;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int n = chunk_qtiles<ROWS>(a, ch);
+    const int un = a.cls_units[ch + nch * it.b];
+    if (r < n) {
+      it.chunk = ch;
+      it.tile = r;
+      it.start = base + int64_t(r) * un;
+      it.units = un;
+      return it;
+    }
+    r -= n;
+    base += int64_t(n) * un;
+  }
+  return it;
+}
+
+// First unit of workgroup range v, and the range holding unit u.
+__device__ __forceinline__ int64_t lean_range_start(const AttnArgs& a, int v) {
+  return int64_t(v) * a.lean_units / a.lean_ctas;
+}
+__device__ __forceinline__ int lean_range_of(const AttnArgs& a, int64_t u) {
+  return int(((u + 1) * a.lean_ctas - 1) / a.lean_units);
+}
+// Workgroup blockIdx.x runs range v: the ranges of one XCD (workgroups are
+// dealt to the 8 XCDs round robin) are consecutive, so the items of a head
+// mostly stay in one L2.
+__device__ __forceinline__ int lean_range_index() {
+  const int c = blockIdx.x, G = gridDim.x;
+  return (G % kXcds == 0) ? (c % kXcds) * (G / kXcds) + c / kXcds : c;
+}
 
 template <int D, typename QKT>
 __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
@@ -352,19 +468,29 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lead = wave < 4;  // MFMA phase first
   const int hl = lane >> 5, l32 = lane & 31;
-  const WorkItem wi = attn_work_item(a);
-  const int head = wi.head, bz = wi.bz;
-  const QueryTile qt = query_tile<kRowsBf16>(a, wi.qtile);
-  if (qt.row_lo >= qt.row_end) return;  // an empty tile of a partial last chunk
-  const int b = bz / a.splits, split = bz % a.splits;
+
+  // One segment: the visits [vis_lo, vis_hi) of key tiles [t_begin, t_end)
+  // of query tile qtile of (stream b, head), written as the output or as
+  // normalised fp32 partials (row r of the tile at part row prow + r).
+  struct Segment {
+    int head, b, qtile, t_begin, t_end;
+    int vis_lo, vis_hi;  // vis_hi = INT_MAX: to the end of the range
+    bool partial;
+    int64_t prow;
+  };
+  auto run_segment = [&](const Segment& sg) __attribute__((always_inline)) {
+  const int head = sg.head, b = sg.b;
+  int t_begin = sg.t_begin, t_end = sg.t_end;
+  const int vis_lo = sg.vis_lo, vis_hi = sg.vis_hi;
+  const bool partial = sg.partial;
+  const int64_t prow = sg.prow;
+  const QueryTile qt = query_tile<kRowsBf16>(a, sg.qtile);
+  if (qt.row_lo >= qt.row_end) return;  // an empty tile of a partial last chunk (grid schedule)
   const int qrow = qt.row_lo + wave * 32 + l32;
   const bool qvalid = qrow < qt.row_end;
 
   // frame slots every query of this workgroup may see (wave-uniform)
   const uint64_t slots = chunk_slot_mask(a, b, qt.chunk);
-
-  const int t_begin = split * a.tiles_per_split;
-  const int t_end = min(t_begin + a.tiles_per_split, a.tiles_total);
 
   // ---- global -> LDS tile copies ----
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
@@ -562,6 +688,27 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     const uint64_t hi = s_hi >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (s_hi + 1)) - 1);
     dense = ((hi & ~((uint64_t(1) << s_lo) - 1)) & ~slots) == 0;
   }
+  // A segment of the balanced schedule: narrow [t_begin, t_end) to the
+  // tiles of visits vis_lo .. vis_hi - 1.
+  if (vis_lo > 0 || vis_hi != INT_MAX) {
+    int t_lo, t_hi = t_end;
+    if (dense) {
+      const int n = t_end - t_begin;
+      t_lo = t_begin + min(vis_lo, n);
+      if (vis_hi != INT_MAX) t_hi = t_begin + min(vis_hi, n);
+    } else {
+      RunWalk w2 = walk;
+      w2.skip(g, slots, vis_lo);
+      t_lo = w2.valid ? w2.t : t_end;
+      if (vis_hi != INT_MAX) {
+        w2.skip(g, slots, vis_hi - vis_lo);
+        if (w2.valid) t_hi = w2.t;
+      }
+    }
+    t_begin = t_lo;
+    t_end = max(t_lo, t_hi);
+    walk.init(g, slots, t_begin, t_end);
+  }
   // One key loop, instantiated twice: without any masking code when every
   // tile of the split is fully visible, and with masks otherwise.
   auto key_loop = [&](auto masked_tag) {
@@ -654,7 +801,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
   if (!qvalid) return;
-  if (a.splits == 1) {
+  if (!partial) {
     __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(b) * a.Nq + qrow) * g.H + head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -673,7 +820,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     }
     if (a.lse && hl == 0) a.lse[(int64_t(b) * g.H + head) * a.Nq + qrow] = lse_v;
   } else {
-    float* pp = a.part_o + (((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow) * D;
+    float* pp = a.part_o + (prow + qrow) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -683,7 +830,61 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
                                                           o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
       }
     }
-    if (hl == 0) a.part_lse[((int64_t(split) * g.B + b) * g.H + head) * a.Nq + qrow] = lse_v;
+    if (hl == 0) a.part_lse[prow + qrow] = lse_v;
+  }
+  };  // run_segment
+
+  // Grid schedule: one segment per workgroup (a query tile against one key
+  // split).  Balanced schedule: the items the workgroup's unit range
+  // [lo, hi) touches -- at most two, as the host keeps ranges no longer
+  // than the shortest item -- the later one first: its segment starts that
+  // item while the earlier one's ends its item, so neighbouring workgroups
+  // walk the same key tiles at the same time.  Two straight-line segments
+  // rather than a loop: inside a loop nest the compiler gives the key loop
+  // too few registers to keep its fragment reads in flight.
+  Segment sg;
+  const bool lean = a.lean != 0;
+  int lean_v = 0;
+  int64_t lean_lo = 0, lean_hi = 0, first_start = 0;
+  if (!lean) {
+    const WorkItem wi = attn_work_item(a);
+    const int split = wi.bz % a.splits;
+    sg.head = wi.head;
+    sg.b = wi.bz / a.splits;
+    sg.qtile = wi.qtile;
+    sg.t_begin = split * a.tiles_per_split;
+    sg.t_end = min(sg.t_begin + a.tiles_per_split, a.tiles_total);
+    sg.vis_lo = 0;
+    sg.vis_hi = INT_MAX;
+    sg.partial = a.splits > 1;
+    sg.prow = ((int64_t(split) * g.B + sg.b) * g.H + sg.head) * a.Nq;
+  } else {
+    lean_v = lean_range_index();
+    lean_lo = lean_range_start(a, lean_v);
+    lean_hi = lean_range_start(a, lean_v + 1);
+    if (lean_hi <= lean_lo) return;
+  }
+  auto lean_segment = [&](int64_t u) {  // the segment of the item holding unit u
+    const LeanItem it = lean_item_at<kRowsBf16>(a, u);
+    sg.head = it.head;
+    sg.b = it.b;
+    sg.qtile = it.chunk * a.qtiles_per_chunk + it.tile;
+    sg.t_begin = 0;
+    sg.t_end = a.tiles_total;
+    sg.vis_lo = int(max(it.start, lean_lo) - it.start);
+    // the item's last segment takes every remaining visit
+    sg.vis_hi = it.start + it.units <= lean_hi ? INT_MAX : int(lean_hi - it.start);
+    sg.partial = sg.vis_lo > 0 || sg.vis_hi != INT_MAX;
+    const int slot = it.start <= lean_lo ? 0 : 1;
+    sg.prow = (int64_t(lean_v) * 2 + slot) * kRowsBf16 - query_tile<kRowsBf16>(a, sg.qtile).row_lo;
+    first_start = it.start;
+  };
+  if (lean) lean_segment(lean_hi - 1);
+  run_segment(sg);
+  if (lean && first_start > lean_lo) {
+    lean_segment(first_start - 1);
+    __syncthreads();  // every wave is done with the first segment's LDS tiles
+    run_segment(sg);
   }
 }
 
@@ -925,10 +1126,110 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   if (a.lse && dg == 0) a.lse[row] = lse;
 }
 
+// ---------------------------------------------------------------------------
+// Balanced-schedule merge: an item whose units span several workgroup
+// ranges left one normalised partial per non-empty range (slot 0 in every
+// range but the first, where it is slot 1 unless the item starts the
+// range); lse = log sum exp(lse_s), O = sum exp(lse_s - lse) O_s, taken in
+// one pass with a running maximum.  Workgroup = 32 query rows of one item
+// (blockIdx.y = row block); each thread owns 16 values of one row.  The
+// item's partial rows are listed once per workgroup (up to 64 at a time).
+// Items done by a single range were written by the attention kernel.
+// ---------------------------------------------------------------------------
+constexpr int kMergeRows = 32;
+template <int D>
+__global__ __launch_bounds__(256) void attn_lean_merge_kernel(AttnArgs a) {
+  constexpr int TPR = 256 / kMergeRows;  // threads per row
+  constexpr int NV = D / 4 / TPR;        // float4 per thread
+  const Geometry& g = a.g;
+  const LeanItem it = lean_item_by_index<kRowsBf16>(a, blockIdx.x);
+  const int c_first = lean_range_of(a, it.start);
+  const int c_last = lean_range_of(a, it.start + it.units - 1);
+  if (c_first == c_last) return;
+  const QueryTile qt = query_tile<kRowsBf16>(a, it.chunk * a.qtiles_per_chunk + it.tile);
+  const int r = blockIdx.y * kMergeRows + threadIdx.x / TPR;  // row in the tile
+  if (blockIdx.y * kMergeRows >= qt.row_end - qt.row_lo) return;
+  const bool rvalid = r < qt.row_end - qt.row_lo;
+  const int j0 = threadIdx.x % TPR;
+  __shared__ int64_t part[64];
+  __shared__ int n_part;
+  const int first_slot = it.start == lean_range_start(a, c_first) ? 0 : 1;
+  float m = -INFINITY, sum = 0.f;
+  float4 acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = c_first; c0 <= c_last; c0 += 64) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int n = 0;
+      int64_t lo = lean_range_start(a, c0);
+      for (int c = c0; c <= min(c_last, c0 + 63); ++c) {
+        const int64_t hi = lean_range_start(a, c + 1);
+        if (hi > lo) part[n++] = (int64_t(c) * 2 + (c == c_first ? first_slot : 0)) * kRowsBf16;  // ranges with no unit wrote nothing
+        lo = hi;
+      }
+      n_part = n;
+    }
+    __syncthreads();
+    if (!rvalid) continue;
+    const int n = n_part;
+    for (int k = 0; k < n; ++k) {
+      const int64_t pr = part[k] + r;
+      const float l = a.part_lse[pr];
+      float4 x[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) x[v] = *reinterpret_cast<const float4*>(a.part_o + pr * D + 4 * (j0 + TPR * v));
+      if (l == -INFINITY) continue;
+      const float m_new = fmaxf(m, l);
+      const float sc = __expf(m - m_new);  // 0 while m is -inf
+      const float w = __expf(l - m_new);
+      sum = sum * sc + w;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        acc[v].x = acc[v].x * sc + w * x[v].x;
+        acc[v].y = acc[v].y * sc + w * x[v].y;
+        acc[v].z = acc[v].z * sc + w * x[v].z;
+        acc[v].w = acc[v].w * sc + w * x[v].w;
+      }
+      m = m_new;
+    }
+  }
+  if (!rvalid) return;
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  const int q = qt.row_lo + r;
+  __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(it.b) * a.Nq + q) * g.H + it.head) * D;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const __bf16 v0 = static_cast<__bf16>(acc[v].x * inv), v1 = static_cast<__bf16>(acc[v].y * inv);
+    const __bf16 v2 = static_cast<__bf16>(acc[v].z * inv), v3 = static_cast<__bf16>(acc[v].w * inv);
+    uint2 w;
+    w.x = uint32_t(__builtin_bit_cast(uint16_t, v0)) | (uint32_t(__builtin_bit_cast(uint16_t, v1)) << 16);
+    w.y = uint32_t(__builtin_bit_cast(uint16_t, v2)) | (uint32_t(__builtin_bit_cast(uint16_t, v3)) << 16);
+    *reinterpret_cast<uint2*>(op + 4 * (j0 + TPR * v)) = w;
+  }
+  if (a.lse && j0 == 0) a.lse[(int64_t(it.b) * g.H + it.head) * a.Nq + q] = sum > 0.f ? m + __logf(sum) : -INFINITY;
+}
+
 }  // namespace
 
+hipError_t launch_attn_lean_merge(const AttnArgs& a, hipStream_t s) {
+  const int nch = a.n_qtiles / a.qtiles_per_chunk;
+  int per_head = 0;
+  for (int ch = 0; ch < nch; ++ch)
+    per_head += (std::min(a.rows_per_chunk, a.Nq - ch * a.rows_per_chunk) + kRowsBf16 - 1) / kRowsBf16;
+  dim3 grid(unsigned(per_head * a.g.H * a.g.B), kRowsBf16 / kMergeRows);
+  if (a.g.D == 128)
+    hipLaunchKernelGGL(attn_lean_merge_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_lean_merge_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_qtiles, a.g.H, a.g.B * a.splits);  // n_qtiles from attn_rows_per_workgroup()
+  // grid schedule: one workgroup per (query tile, head, stream * splits);
+  // balanced schedule: lean_ctas workgroups over the unit ranges
+  if (a.lean && (a.g.dtype != SCV_BF16 || a.lean_ctas < 1)) return hipErrorInvalidValue;
+  dim3 grid = a.lean ? dim3(unsigned(a.lean_ctas)) : dim3(a.n_qtiles, a.g.H, a.g.B * a.splits);
   if (a.g.dtype == SCV_BF16) {
     const bool f16 = a.g.qk_dtype == SCV_FP16;
     if (a.g.D == 128) {

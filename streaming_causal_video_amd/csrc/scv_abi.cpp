@@ -2,6 +2,7 @@
 // cache layout, per-cache constants and kernel launches.  Every entry point
 // validates before enqueueing anything and never lets an exception escape.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -238,18 +239,113 @@ int64_t seen_frames(const scv_cache* c, int64_t s_c) {
   return std::min<int64_t>(c->g.n_slots, sink + std::max<int64_t>(0, end - lo));
 }
 
-// Key splits for a request.  kv_splits > 0 is taken as given (capped at 64
-// and at the tile count).  Otherwise a makespan model picks one: workgroups
-// of each (stream, chunk) class visit their visible key tiles (from t0 when
-// given, else the steady state), split s ways -- a split may hold up to all
-// of a class's tiles, at most tiles/s of them; they run in rounds over the
-// compute units, each round as long as the longest workgroup plus a fixed
-// 3-tile start/drain cost; with splits the fp32 partials are written and
-// read back by the merge (at ~8.5 MB per tile-time, plus 2 tile-times for
-// the extra launch).  Only split counts whose workspace fits ws_limit count.
+// Key tiles a query chunk starting at frame s_c visits when the cache holds
+// every frame the sink and window rules keep for it: the tiles holding a key
+// of a visible slot (at least 1, so that every item of the balanced
+// schedule owns a unit and gets its output written).
+int visited_tiles(const scv_cache* c, int64_t s_c) {
+  const scv::Geometry& g = c->g;
+  const int64_t end = s_c + g.C;
+  uint64_t mask = 0;
+  for (int j = 0; j < g.S_f && j < end; ++j) mask |= uint64_t(1) << j;
+  const int64_t lo = std::max<int64_t>(std::max<int64_t>(g.S_f, s_c - g.W), std::max<int64_t>(0, end - g.R));
+  for (int64_t f = lo; f < end; ++f) mask |= uint64_t(1) << (g.S_f + int(f % g.R));
+  const int64_t tiles = g.rows_pad / scv::kKeyTile;
+  int64_t count = 0, prev_hi = -1;
+  for (int s = 0; s < g.n_slots;) {
+    if (!((mask >> s) & 1)) {
+      ++s;
+      continue;
+    }
+    int s1 = s;
+    while (s1 < g.n_slots && ((mask >> s1) & 1)) ++s1;
+    const int64_t r_lo = int64_t(s) * g.slot_rows, r_hi = int64_t(s1 - 1) * g.slot_rows + g.P;
+    int64_t t_lo = r_lo / scv::kKeyTile;
+    const int64_t t_hi = std::min<int64_t>((r_hi - 1) / scv::kKeyTile, tiles - 1);
+    if (t_lo <= prev_hi) t_lo = prev_hi + 1;  // a tile shared by two runs counts once
+    if (t_hi >= t_lo) count += t_hi - t_lo + 1;
+    prev_hi = std::max(prev_hi, t_hi);
+    s = s1;
+  }
+  return int(std::max<int64_t>(1, count));
+}
+
+// The balanced schedule needs the bf16 kernel and unit counts that fit int16.
+bool lean_possible(const scv_cache* c) {
+  return c->g.dtype == SCV_BF16 && c->g.rows_pad / scv::kKeyTile <= 32767;
+}
+
+size_t lean_workspace_bytes(const scv_cache* c, int ctas) {
+  const size_t rows = size_t(ctas) * 2 * scv::kAttnRowsBf16;
+  return align_up(rows * c->g.D * 4, 256) + align_up(rows * 4, 256);
+}
+
+// Units per item of each (stream, chunk) class, class id ch + n_chunks * b:
+// visited key tiles from t0, or the steady state for every stream without.
+void class_units(const scv_cache* c, const int64_t* t0, int32_t n_frames, int16_t* out) {
+  const int nch = (n_frames + c->g.C - 1) / c->g.C;
+  const int steady = visited_tiles(c, int64_t(c->g.S_f) + c->g.W + c->g.R);
+  for (int b = 0; b < c->g.B; ++b)
+    for (int ch = 0; ch < nch; ++ch)
+      out[ch + nch * b] = int16_t(t0 ? visited_tiles(c, t0[b] + int64_t(ch) * c->g.C) : steady);
+}
+
+// The balanced schedule's work: total units and workgroup count.  The
+// workgroups are a multiple k of the compute units (so that equal ranges
+// fill whole rounds), with k the smallest that keeps every range no longer
+// than the shortest item: a range then touches at most two items, which is
+// all the kernel handles.
+constexpr int64_t kMaxLeanRounds = 16;
+struct LeanPlan {
+  int64_t units;
+  int ctas;
+};
+LeanPlan lean_plan(const scv_cache* c, int32_t n_frames, const int16_t* units) {
+  const int rows = scv::kAttnRowsBf16;
+  const int64_t nq = int64_t(n_frames) * c->g.P;
+  const int64_t rows_per_chunk = std::min<int64_t>(int64_t(c->g.C) * c->g.P, nq);
+  const int nch = (n_frames + c->g.C - 1) / c->g.C;
+  int64_t total = 0, shortest = INT64_MAX;
+  for (int b = 0; b < c->g.B; ++b)
+    for (int ch = 0; ch < nch; ++ch) {
+      const int64_t rows_ch = std::min<int64_t>(rows_per_chunk, nq - int64_t(ch) * rows_per_chunk);
+      const int64_t u = units[ch + nch * b];
+      total += ((rows_ch + rows - 1) / rows) * c->g.H * u;
+      shortest = std::min(shortest, u);
+    }
+  const int64_t cus = device_cu_count();
+  const int64_t k = std::max<int64_t>(1, (total + cus * shortest - 1) / (cus * shortest));
+  LeanPlan p;
+  p.units = total;
+  p.ctas = k <= kMaxLeanRounds ? int(k * cus) : 0;  // 0: items too short for the balanced schedule
+  return p;
+}
+
+// Schedule for a request: a key split count >= 1 (grid schedule) or -1 (the
+// balanced schedule).  kv_splits > 0 is taken as given (capped at 64 and at
+// the tile count); kv_splits = -1 asks for the balanced schedule (the fp32
+// path runs the grid schedule unsplit).  With kv_splits = 0 a makespan model
+// picks the cheapest option whose workspace fits ws_limit.  Grid schedule:
+// workgroups of each (stream, chunk) class visit their visible key tiles
+// (from t0 when given, else the steady state), split s ways -- a split may
+// hold up to all of a class's tiles, at most tiles/s of them; they run in
+// rounds over the compute units, each round as long as the longest
+// workgroup plus a fixed 3-tile start/drain cost; with splits the fp32
+// partials are written and read back by the merge (at ~8.5 MB per
+// tile-time, plus 2 tile-times for the extra launch).  Balanced schedule:
+// every compute unit runs an equal share of all units plus the fixed cost of
+// two segments, then the merge reads back up to two partials per range.
 int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t requested, size_t ws_limit) {
   const int tiles = int(c->g.rows_pad / scv::kKeyTile);
   if (requested > 0) return std::max(1, std::min(std::min(requested, tiles), 64));
+  int16_t units[scv::kMaxBatch * scv::kMaxQueryChunks];
+  LeanPlan plan{0, 0};
+  if (lean_possible(c)) {
+    class_units(c, t0, n_frames, units);
+    plan = lean_plan(c, n_frames, units);
+  }
+  const bool lean_ok = plan.ctas > 0;
+  if (requested == -1) return lean_ok ? -1 : 1;
   const int rows = scv::attn_rows_per_workgroup(c->g);
   const int64_t nq = int64_t(n_frames) * c->g.P;
   const int64_t rows_per_chunk = std::min<int64_t>(int64_t(c->g.C) * c->g.P, nq);
@@ -287,10 +383,28 @@ int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int3
       best_s = s;
     }
   }
+  if (lean_ok) {
+    const LeanPlan& p = plan;
+    const double rounds = double(p.ctas / cus);
+    const double per = std::ceil(double(p.units) / p.ctas);
+    const double partial_bytes = 4.0 * p.ctas * rows * (4.0 * c->g.D + 4.0);
+    // a segment's fixed cost (Q loads, pipeline fill and drain, partial
+    // write) measured at ~7 tile-times
+    const double cost = rounds * (per + 2.0 * 7.0) + 2.0 + partial_bytes / 8.5e6;
+    if (cost < best && lean_workspace_bytes(c, p.ctas) <= ws_limit) return -1;
+  }
   return best_s;
 }
 
+// Workgroups of the balanced schedule (t0 null: the steady state).
+int lean_ctas(const scv_cache* c, const int64_t* t0, int32_t n_frames) {
+  int16_t units[scv::kMaxBatch * scv::kMaxQueryChunks];
+  class_units(c, t0, n_frames, units);
+  return lean_plan(c, n_frames, units).ctas;
+}
+
 size_t workspace_bytes(const scv_cache* c, int32_t n_frames, int splits) {
+  if (splits < 0) return lean_workspace_bytes(c, lean_ctas(c, nullptr, n_frames));
   if (splits <= 1) return 0;
   const size_t rows = size_t(c->g.B) * c->g.H * size_t(n_frames) * c->g.P;
   return align_up(size_t(splits) * rows * c->g.D * 4, 256) + align_up(size_t(splits) * rows * 4, 256);
@@ -586,7 +700,7 @@ scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, con
 int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
                              size_t ws_bytes) {
   try {
-    if (!c || n_frames < 1 || kv_splits < 0) return 0;
+    if (!c || n_frames < 1 || kv_splits < -1) return 0;
     if (t0 && check_times(c, t0, n_frames) != SCV_OK) return 0;
     return resolve_splits(c, t0, n_frames, kv_splits, ws_bytes);
   } catch (...) {
@@ -596,8 +710,21 @@ int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_fr
 
 size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits) {
   try {
-    if (!c || n_frames < 1 || kv_splits < 0) return 0;
+    if (!c || n_frames < 1 || kv_splits < -1) return 0;
     return workspace_bytes(c, n_frames, resolve_splits(c, nullptr, n_frames, kv_splits, SIZE_MAX));
+  } catch (...) {
+    return 0;
+  }
+}
+
+size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* t0, int32_t n_frames,
+                                             int32_t kv_splits) {
+  try {
+    if (!c || !t0 || n_frames < 1 || kv_splits < -1) return 0;
+    if (check_times(c, t0, n_frames) != SCV_OK) return 0;
+    const int splits = resolve_splits(c, t0, n_frames, kv_splits, SIZE_MAX);
+    if (splits >= 0) return workspace_bytes(c, n_frames, splits);
+    return lean_workspace_bytes(c, lean_ctas(c, t0, n_frames));
   } catch (...) {
     return 0;
   }
@@ -613,11 +740,17 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
     if ((s = check_ptr(lse, "lse", false)) != SCV_OK) return s;
     if (n_frames < 1 || n_frames > c->g.k_max * c->g.C)
       return fail(SCV_E_SHAPE, "n_frames must be in [1, max_query_chunks*chunk_frames]");
-    if (kv_splits < 0) return fail(SCV_E_INVALID, "kv_splits must be >= 0");
+    if (kv_splits < -1) return fail(SCV_E_INVALID, "kv_splits must be >= -1");
     if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
     // with kv_splits = 0 the choice sees t0 and the workspace given
     const int splits = resolve_splits(c, t0, n_frames, kv_splits, ws ? ws_bytes : 0);
-    const size_t need = workspace_bytes(c, n_frames, splits);
+    int16_t lean_units[scv::kMaxBatch * scv::kMaxQueryChunks];
+    LeanPlan plan{0, 0};
+    if (splits < 0) {
+      class_units(c, t0, n_frames, lean_units);
+      plan = lean_plan(c, n_frames, lean_units);
+    }
+    const size_t need = splits < 0 ? lean_workspace_bytes(c, plan.ctas) : workspace_bytes(c, n_frames, splits);
     if (need > 0) {
       if (!ws) return fail(SCV_E_WORKSPACE, "workspace is NULL; need " + std::to_string(need) + " bytes");
       if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SCV_E_ALIGN, "workspace must be 256-byte aligned");
@@ -642,7 +775,8 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
       a.qtiles_per_chunk = (std::min(a.rows_per_chunk, a.Nq) + rows_wg - 1) / rows_wg;
       a.n_qtiles = ((n_frames + c->g.C - 1) / c->g.C) * a.qtiles_per_chunk;
     }
-    a.splits = splits;
+    const bool lean = splits < 0;
+    a.splits = lean ? 1 : splits;
     {
       // work classes (chunk, stream), longest first: the keys each chunk can
       // see once its history is in the cache (ties keep their natural order)
@@ -666,9 +800,20 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
       a.part_o = static_cast<float*>(ws);
       a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(splits) * rows * c->g.D * 4, 256));
     }
+    if (lean) {
+      std::memcpy(a.cls_units, lean_units, sizeof(lean_units));
+      a.lean = 1;
+      a.lean_ctas = plan.ctas;
+      a.lean_units = plan.units;
+      a.part_o = static_cast<float*>(ws);
+      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                            align_up(size_t(plan.ctas) * 2 * scv::kAttnRowsBf16 * c->g.D * 4, 256));
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((s = hip_status(scv::launch_chunk_attention(a, st), "chunk_attention launch")) != SCV_OK) return s;
-    if (splits > 1) {
+    if (lean) {
+      if ((s = hip_status(scv::launch_attn_lean_merge(a, st), "attn_lean_merge launch")) != SCV_OK) return s;
+    } else if (splits > 1) {
       scv::MergeArgs m;
       m.part_o = a.part_o;
       m.part_lse = a.part_lse;

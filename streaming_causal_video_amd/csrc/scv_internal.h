@@ -112,6 +112,19 @@ struct AttnArgs {
   // (chunk, stream) work classes, class id = chunk + n_chunks * stream, in
   // the order workgroups should start (longest first)
   int16_t cls_order[kMaxBatch * kMaxQueryChunks];
+  // Balanced schedule (lean != 0, bf16 kernel only).  Work units are
+  // (query tile, visited key tile) pairs; the items (stream, head, chunk,
+  // query tile) are laid end to end, stream-major, then head, chunk and
+  // tile, each taking cls_units[chunk + n_chunks * stream] units.  The grid
+  // has lean_ctas workgroups; workgroup v (after the XCD renumbering) takes
+  // units [v * lean_units / lean_ctas, (v + 1) * lean_units / lean_ctas).
+  // An item cut by a range boundary leaves normalised fp32 partials in
+  // part_o / part_lse at [v][slot][row] (slot 0: the workgroup's first item,
+  // 1: its last) for attn_lean_merge_kernel.
+  int32_t lean;
+  int32_t lean_ctas;
+  int64_t lean_units;
+  int16_t cls_units[kMaxBatch * kMaxQueryChunks];
 };
 
 struct MergeArgs {
@@ -145,5 +158,6 @@ hipError_t launch_qkv_rope(const QkvArgs& a, hipStream_t s);
 hipError_t launch_cache_reset(const Geometry& g, void* kv_base, size_t kv_bytes, int64_t* stamps, hipStream_t s);
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_attn_lean_merge(const AttnArgs& a, hipStream_t s);
 
 }  // namespace scv

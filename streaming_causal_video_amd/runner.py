@@ -42,7 +42,7 @@ class StreamRunner:
         self.o = torch.empty(shape, dtype=tdt, device=device)
         self.lse = torch.empty((w.batch, w.heads, nq * w.tokens_per_frame), dtype=torch.float32, device=device) \
             if with_lse else None
-        self.ws = self.cache.make_workspace(nq, kv_splits)
+        self.ws = self.cache.make_workspace(nq, kv_splits, t0=w.t0)
         ws_bytes = 0 if self.ws is None else self.ws.numel()
         self.splits = self.cache.attention_splits(nq, kv_splits, t0=w.t0, ws_bytes=ws_bytes)
 

@@ -182,7 +182,9 @@ def test_attention_validation(lib):
     assert lib.scv_chunk_attention(h, q, t0(1000), 0, q, None, 1, None, 0, None) == -2
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, None, None, 1, None, 0, None) == -1
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, q + 4, 1, None, 0, None) == -4
-    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -1, None, 0, None) == -1
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -2, None, 0, None) == -1
+    # the balanced schedule needs its workspace
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -1, None, 0, None) == -7
     need = lib.scv_attention_workspace_bytes(h, 3, 4)
     assert need > 0
     assert lib.scv_attention_splits(h, None, 3, 4, (1 << 64) - 1) == 4
@@ -247,16 +249,58 @@ def test_sink_update_validation(lib):
 
 
 def test_auto_splits_respect_workspace_and_t0(lib):
-    # 720p, one stream: the steady-state choice splits; without workspace it
-    # cannot; a stream at t0 = 0 sees only its own chunk
+    # 720p, one stream: the steady-state choice is the balanced schedule;
+    # without workspace it runs unsplit; with only a split-sized workspace
+    # it splits
     cfg, h = make_handle(lib, grid_h=45, grid_w=80, window_frames=8)
     big = (1 << 64) - 1
     s_steady = lib.scv_attention_splits(h, None, 3, 0, big)
-    assert s_steady > 1
+    assert s_steady == -1
     assert lib.scv_attention_workspace_bytes(h, 3, 0) > 0
     assert lib.scv_attention_splits(h, None, 3, 0, 0) == 1
     assert lib.scv_attention_splits(h, t0(20000), 3, 0, big) == s_steady
     assert lib.scv_attention_splits(h, t0(-1), 3, 0, big) == 0
+    assert lib.scv_attention_splits(h, t0(20000), 3, -2, big) == 0
+    lean = lib.scv_attention_workspace_bytes(h, 3, -1)
+    assert lean > 0
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean) == -1
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean - 1) > 1  # key splits that fit
+    lib.scv_cache_destroy(h)
+
+
+def lean_ws(ctas, d=128):
+    rows = ctas * 2 * 256
+    return -(-(rows * d * 4) // 256) * 256 + -(-(rows * 4) // 256) * 256
+
+
+def test_balanced_schedule_plan(lib):
+    # Without a GPU the library assumes 256 compute units.
+    big = (1 << 64) - 1
+    # 480p layer: 12 heads x 19 query tiles = 228 workgroups of 390 key
+    # tiles leave 28 of 256 compute units idle; the balanced schedule cuts
+    # 228 * 390 units into 256 ranges of <= 348 (< 390: two items at most)
+    cfg, h = make_handle(lib)
+    assert lib.scv_attention_splits(h, t0(1000), 3, 0, big) == -1
+    assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, 0) == lean_ws(256)
+    assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, -1) == lean_ws(256)
+    assert lib.scv_attention_workspace_bytes(h, 3, -1) == lean_ws(256)
+    # forced splits keep the grid schedule
+    assert lib.scv_attention_splits(h, t0(1000), 3, 2, big) == 2
+    lib.scv_cache_destroy(h)
+    # 14B layer (40 heads, 760 workgroups = 2.97 rounds): the grid schedule
+    # already fills three rounds; the balanced one would need 768 ranges
+    cfg, h = make_handle(lib, heads=40)
+    assert lib.scv_attention_splits(h, t0(1000), 3, 0, big) == 1
+    assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, -1) == lean_ws(768)
+    lib.scv_cache_destroy(h)
+    # 720p: 516 items of 675 tiles -> 3 ranges per compute unit (453.5 units)
+    cfg, h = make_handle(lib, grid_h=45, grid_w=80, window_frames=8)
+    assert lib.scv_attention_request_workspace_bytes(h, t0(20000), 3, 0) == lean_ws(768)
+    lib.scv_cache_destroy(h)
+    # fp32 has no balanced kernel: -1 falls back to one split
+    cfg, h = make_handle(lib, dtype="fp32", head_dim=64, split=(24, 20, 20))
+    assert lib.scv_attention_splits(h, t0(37), 2, -1, big) == 1
+    assert lib.scv_attention_workspace_bytes(h, 2, -1) == 0
     lib.scv_cache_destroy(h)
 
 

@@ -190,6 +190,66 @@ def test_split_kv_720p(gpu_lib):
     check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, 7, n_random=96))
 
 
+BALANCED = [w for w in SMALL if w.dtype == "bf16"] + [
+    small("balanced-multichunk", batch=2, grid_h=4, grid_w=8, window_frames=3, max_query_chunks=3, t0=(2, 40),
+          seed=141),
+    # several query tiles per head (ragged last tile), ranges that cut items
+    small("balanced-tiles", heads=3, grid_h=15, grid_w=26, chunk_frames=2, window_frames=4, t0=(31,), seed=142),
+]
+
+
+@pytest.mark.parametrize("w", BALANCED, ids=lambda w: w.name)
+def test_balanced_small(w, gpu_lib):
+    """The balanced schedule (equal unit ranges, partials merged) against
+    the oracle, and against the grid schedule's unsplit output."""
+    say(f"case balanced {w.name}")
+    r = run_gpu(w, kv_splits=-1)
+    assert r.splits == -1
+    oc, q_rot = oracle_replay(w)
+    check_attention(r, oc, q_rot, w)
+    r1 = run_gpu(w, kv_splits=1)
+    o1 = to_np(r1.o)
+    d = np.max(np.abs(to_np(r.o) - o1))
+    say(f"  balanced vs unsplit max-abs {d:.3e}")
+    # the merged fp32 partials round to bf16 on their own: outputs may differ
+    # by a bf16 rounding step at the largest magnitude (2^-7 relative)
+    assert d <= 2.0 ** -7 * max(1.0, float(np.max(np.abs(o1))))
+
+
+@pytest.mark.parametrize("w", [W.WAN13B_480P_B4, W.WAN14B_480P, W.WAN13B_480P_PREFILL, W.WAN13B_480P_CHUNKS4],
+                         ids=lambda w: w.name)
+def test_balanced_workloads(w, gpu_lib):
+    """Full-size workloads under the balanced schedule (items of different
+    lengths, several rounds of ranges), on sampled rows."""
+    say(f"case balanced {w.name}")
+    r = run_gpu(w, kv_splits=-1)
+    say(f"  gpu done (splits={r.splits}); oracle replay")
+    assert r.splits == -1
+    oc, q_rot = oracle_replay(w)
+    check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, w.seed, n_random=48))
+
+
+def test_balanced_empty_cache(gpu_lib):
+    """Ranges over a cache with nothing visible: O = 0, lse = -inf."""
+    import torch
+
+    from streaming_causal_video_amd import binding as B
+
+    w = small("empty-balanced", grid_h=8, grid_w=8)
+    say("case balanced empty cache")
+    cache = B.Cache(B.config_for(w))
+    cache.cache_init()
+    P = w.tokens_per_frame
+    shape = (1, 2 * P, 2, 128)
+    q = torch.ones(shape, dtype=torch.bfloat16, device="cuda")
+    o = torch.full(shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 2, 2 * P), dtype=torch.float32, device="cuda")
+    cache.chunk_attention(q, [9], 2, o, lse, kv_splits=-1)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert torch.all(torch.isneginf(lse))
+
+
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[3], SMALL[4], SMALL[-1]], ids=lambda w: w.name)
 def test_unfused_equals_fused(w, gpu_lib):
     import torch
