@@ -391,7 +391,11 @@ int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int3
     // a segment's fixed cost (Q loads, pipeline fill and drain, partial
     // write) measured at ~7 tile-times
     const double cost = rounds * (per + 2.0 * 7.0) + 2.0 + partial_bytes / 8.5e6;
-    if (cost < best && lean_workspace_bytes(c, p.ctas) <= ws_limit) return -1;
+    // Only a clear win moves off the grid schedule: with every compute unit
+    // busy the shader clock drops a few percent (measured ~3% on the 480p
+    // layer, which then runs no faster balanced), and the balanced
+    // schedule reads more K/V from HBM.
+    if (cost < 0.95 * best && lean_workspace_bytes(c, p.ctas) <= ws_limit) return -1;
   }
   return best_s;
 }

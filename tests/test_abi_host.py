@@ -278,10 +278,12 @@ def test_balanced_schedule_plan(lib):
     big = (1 << 64) - 1
     # 480p layer: 12 heads x 19 query tiles = 228 workgroups of 390 key
     # tiles leave 28 of 256 compute units idle; the balanced schedule cuts
-    # 228 * 390 units into 256 ranges of <= 348 (< 390: two items at most)
+    # 228 * 390 units into 256 ranges of <= 348 (< 390: two items at most).
+    # The model sees less than the 5% margin it asks for and keeps the grid.
     cfg, h = make_handle(lib)
-    assert lib.scv_attention_splits(h, t0(1000), 3, 0, big) == -1
-    assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, 0) == lean_ws(256)
+    assert lib.scv_attention_splits(h, t0(1000), 3, 0, big) == 1
+    assert lib.scv_attention_splits(h, t0(1000), 3, -1, big) == -1
+    assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, 0) == 0
     assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, -1) == lean_ws(256)
     assert lib.scv_attention_workspace_bytes(h, 3, -1) == lean_ws(256)
     # forced splits keep the grid schedule
