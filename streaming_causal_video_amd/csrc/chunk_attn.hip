@@ -20,6 +20,11 @@
 //    v_mfma_f32_32x32x2_f32, double-buffered LDS tiles staged through VGPRs.
 //  * attn_merge_kernel: combines the normalised fp32 partials of key splits
 //    (lse-weighted).
+//  * Balanced schedule (bf16 kernel): instead of one workgroup per query
+//    tile and key split, the launch's work -- query tile x visited key tile
+//    units -- is cut into equal ranges, one per workgroup, so that every
+//    compute unit runs equally long; attn_lean_merge_kernel combines the
+//    partials of query tiles cut by range boundaries.
 // Shared by both attention kernels:
 //  * S^T = K Q^T on MFMA (A = K rows from LDS, B = the wave's Q in VGPRs),
 //    so each lane holds one query column and 16 of every 32 keys: the row
