@@ -229,6 +229,40 @@ def test_balanced_workloads(w, gpu_lib):
     check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, w.seed, n_random=48))
 
 
+@pytest.mark.parametrize("kv_splits", [-1, 1, 2])
+def test_partial_last_chunk(kv_splits, gpu_lib):
+    """A call of 3 frames with 2-frame chunks: the second query chunk holds
+    one frame (its query tiles are shorter), under every schedule."""
+    import torch
+
+    from streaming_causal_video_amd import binding as B
+
+    w = small("ragged-chunk", grid_h=6, grid_w=10, window_frames=3, max_query_chunks=2, t0=(8,), seed=143)
+    say(f"case partial last chunk kv_splits={kv_splits}")
+    cache = B.Cache(B.config_for(w))
+    oc = O.OracleCache(spec_of(w))
+    sk, sv = G.frames_tensor(w, G.TENSOR_K, [0], 1), G.frames_tensor(w, G.TENSOR_V, [0], 1)
+    cache.cache_init(to_device(sk, "bf16"), to_device(sv, "bf16"))
+    oc.init(sk, sv)
+    wk, wv = G.frames_tensor(w, G.TENSOR_K, [5], 3), G.frames_tensor(w, G.TENSOR_V, [5], 3)
+    cache.rope3d_append(None, None, to_device(wk, "bf16"), to_device(wv, "bf16"), [5], 3)
+    oc.kv_append_roll(oc.rope3d_apply(wk, [5], 3), wv, [5], 3)
+    n = 3
+    q, k, v = (G.frames_tensor(w, t, [8], n) for t in (G.TENSOR_Q, G.TENSOR_K, G.TENSOR_V))
+    shape = (1, n * w.tokens_per_frame, w.heads, w.head_dim)
+    q_rot = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, w.heads, shape[1]), dtype=torch.float32, device="cuda")
+    cache.rope3d_append(to_device(q, "bf16"), q_rot, to_device(k, "bf16"), to_device(v, "bf16"), [8], n)
+    assert cache.attention_splits(n, kv_splits, t0=[8]) == kv_splits
+    cache.chunk_attention(q_rot, [8], n, o, lse, kv_splits=kv_splits)
+    torch.cuda.synchronize()
+    q_ref = oc.rope3d_append(q, k, v, [8], n)
+    O_ref, L_ref = oc.chunk_attention(q_ref, [8], n)
+    check_values("o", to_np(o), O_ref, "bf16")
+    check_values("lse", lse.cpu().numpy().astype(np.float64), L_ref, "bf16")
+
+
 def test_balanced_empty_cache(gpu_lib):
     """Ranges over a cache with nothing visible: O = 0, lse = -inf."""
     import torch
