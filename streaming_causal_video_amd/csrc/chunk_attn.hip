@@ -493,6 +493,11 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   if (qt.row_lo >= qt.row_end) return;  // an empty tile of a partial last chunk (grid schedule)
   const int qrow = qt.row_lo + wave * 32 + l32;
   const bool qvalid = qrow < qt.row_end;
+  // A wave whose 32 rows all lie past the tile's end (the last tile of a
+  // head or chunk) skips its MFMAs and softmax but keeps its share of the
+  // tile loads and every barrier; the idle SIMD time leaves power to the
+  // others.
+  const bool active = qt.row_lo + wave * 32 < qt.row_end;
 
   // frame slots every query of this workgroup may see (wave-uniform)
   const uint64_t slots = chunk_slot_mask(a, b, qt.chunk);
@@ -762,8 +767,8 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
         // the MFMA phase outranks the partner wave's softmax at issue
         __builtin_amdgcn_s_setprio(1);
-        if (have_prev) pv(stp);
-        if (cur) qk(st);
+        if (active && have_prev) pv(stp);
+        if (active && cur) qk(st);
         __builtin_amdgcn_s_setprio(0);
         // each wave's share of tile i+1 has landed before the barrier after
         // which the first reader (a lead wave in M(i+1)) may start; a
@@ -773,7 +778,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         // V(i): the load of tile i+2 goes out here, in the VALU phase, so
         // that its issue never holds up the MFMA phase
         if (tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
-        if (cur) {
+        if (cur && active) {
           if constexpr (kMasked) {
             if (!f0) mask(tq0);
           }
