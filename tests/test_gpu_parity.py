@@ -229,6 +229,33 @@ def test_balanced_workloads(w, gpu_lib):
     check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, w.seed, n_random=48))
 
 
+LIMITS = [
+    # 64 frame slots (sink 1 + window 60 + chunk 3), the most the cache
+    # accepts: slot masks and ballots use every bit; one stream wraps the
+    # ring, one is still filling its window
+    small("max-slots-bf16", batch=2, heads=2, grid_h=2, grid_w=4, chunk_frames=3, window_frames=60, t0=(200, 40),
+          seed=150),
+    small("max-slots-fp32", dtype="fp32", batch=2, heads=2, head_dim=64, split=(24, 20, 20), grid_h=2, grid_w=4,
+          chunk_frames=3, window_frames=60, t0=(131, 7), seed=151),
+    # 64 streams, the most the kernels' argument blocks hold, each at its own t0
+    small("max-batch-bf16", batch=64, heads=1, grid_h=2, grid_w=2, chunk_frames=1, window_frames=2,
+          t0=tuple(range(0, 128, 2)), seed=152),
+]
+
+
+# the host's choice for every case, and the balanced schedule (bf16 only)
+LIMIT_CASES = [(w, 0) for w in LIMITS] + [(w, -1) for w in LIMITS if w.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("w,kv_splits", LIMIT_CASES, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_size_limits(w, kv_splits, gpu_lib):
+    say(f"case limits {w.name} kv_splits={kv_splits}")
+    r = run_gpu(w, kv_splits=kv_splits)
+    oc, q_rot = oracle_replay(w)
+    check_cache_contents(r, oc, w)
+    check_attention(r, oc, q_rot, w)
+
+
 @pytest.mark.parametrize("kv_splits", [-1, 1, 2])
 def test_partial_last_chunk(kv_splits, gpu_lib):
     """A call of 3 frames with 2-frame chunks: the second query chunk holds
