@@ -240,6 +240,12 @@ LIMITS = [
     # 64 streams, the most the kernels' argument blocks hold, each at its own t0
     small("max-batch-bf16", batch=64, heads=1, grid_h=2, grid_w=2, chunk_frames=1, window_frames=2,
           t0=tuple(range(0, 128, 2)), seed=152),
+    # 8 query chunks per call, the most a call takes
+    small("max-chunks-bf16", grid_h=3, grid_w=4, chunk_frames=2, window_frames=3, max_query_chunks=8, t0=(5,),
+          seed=153),
+    # 64 streams x 8 chunks: 512 (stream, chunk) classes, a full class table
+    small("max-classes-bf16", batch=64, heads=1, grid_h=2, grid_w=2, chunk_frames=1, window_frames=1,
+          max_query_chunks=8, t0=tuple(range(0, 192, 3)), seed=154),
 ]
 
 
