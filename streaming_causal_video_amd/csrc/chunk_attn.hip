@@ -594,16 +594,23 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       }
   };
   // O^T += V^T P^T of the tile in stage st
+  // V^T fragment n (in P V order: j, gg, db) of the tile in stage st
+  auto vfrag = [&](const char* st, int n) {
+    const int db = n % DB, jg = n / DB;
+    return *reinterpret_cast<const bf16x8*>(st + voff[jg] + db * 32 * T::VROW);
+  };
+  // The first kLookahead fragments of the next P V are read at the end of
+  // the softmax phase, before the barrier that opens the MFMA phase (their
+  // tile was published a trip earlier), so the matrix core does not wait a
+  // full LDS latency at the start of every MFMA phase.
+  bf16x8 vpre[kLookahead];
   auto pv_ops = [&](const char* st) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + voff[2 * j + gg] + db * 32 * T::VROW);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[j][gg], o[db], 0, 0, 0);
-        }
+    for (int n = 0; n < 4 * DB; ++n) {
+      const int j = n / (2 * DB), gg = (n / DB) % 2, db = n % DB;
+      const bf16x8 v = n < kLookahead ? vpre[n] : vfrag(st, n);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[j][gg], o[db], 0, 0, 0);
+    }
   };
   auto qk = [&](const char* st) {
     qk_ops(st);
@@ -611,7 +618,12 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   };
   auto pv = [&](const char* st) {
     pv_ops(st);
-    interleave(4 * DB);
+    // the reads run kLookahead MFMAs ahead from the first MFMA on
+    for (int i = 0; i < 4 * DB - kLookahead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    for (int i = 0; i < kLookahead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
   // Masks the keys of tile t that no query here may see.  Element i of s[j]
   // in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4) of the tile, that
@@ -783,6 +795,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
             if (!f0) mask(tq0);
           }
           softmax();
+          // the first fragments of this tile's P V, done in the next trip
+#pragma unroll
+          for (int n = 0; n < kLookahead; ++n) vpre[n] = vfrag(st, n);
         }
         if (lead && tq1 < t_end) {
           if (tq2 < t_end)
