@@ -101,7 +101,10 @@ typedef struct scv_config {
                             /* 0 = same as dtype; SCV_FP16 (dtype SCV_BF16   */
                             /* only) keeps 3 more mantissa bits at the same  */
                             /* MFMA rate for inputs whose rotated values     */
-                            /* stay within +-65504                           */
+                            /* stay within +-65504; a rotated value beyond   */
+                            /* that range is stored saturated to +-65504     */
+                            /* (finite: attention stays defined, but such    */
+                            /* keys and queries are no longer exact)         */
 } scv_config;
 
 /* Byte layout of the caller's cache buffer (offsets from its base). */
@@ -157,7 +160,10 @@ scv_status scv_cache_init(scv_cache* c, const void* sink_k, const void* sink_v, 
 scv_status scv_rope3d_apply(const scv_cache* c, void* q, void* k, const int64_t* t0, int32_t n_frames,
                             void* stream);
 
-/* kv_append_roll(chunk).  Writes the already-rotated keys k_rot (qk_dtype)
+/* kv_append_roll(chunk): the rolling KV cache with its sink anchor of the
+ * StreamDiffusionV2 review (section 2: the initial frames' KV stay pinned as
+ * the global anchor, the rest of the cache is a fixed-size window that rolls
+ * forward with the stream).  Writes the already-rotated keys k_rot (qk_dtype)
  * and the values v of frames t0[b] .. t0[b]+n_frames-1 into their slots
  * (sink frames into the pinned sink, later frames into the ring, evicting
  * what the slot held) and stamps the slots.  Among the frames of one call at most R may
@@ -165,7 +171,10 @@ scv_status scv_rope3d_apply(const scv_cache* c, void* q, void* k, const int64_t*
 scv_status scv_kv_append_roll(scv_cache* c, const void* k_rot, const void* v, const int64_t* t0, int32_t n_frames,
                               void* stream);
 
-/* Fused rope3d_apply + kv_append_roll in one kernel: q is rotated into q_rot
+/* Fused rope3d_apply + kv_append_roll in one kernel (the Causal-RoPE SP
+ * paper, section 2(c), fuses RoPE with its neighbouring operator to save
+ * launches and memory passes; here the neighbour is the cache append, one
+ * HBM pass instead of three).  q is rotated into q_rot
  * (qk_dtype; q_rot == q rotates in place), k is rotated and written with v
  * into the cache; k itself is not modified.  q and q_rot may both be NULL
  * (append only). */
@@ -251,7 +260,11 @@ size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32
 size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* t0, int32_t n_frames,
                                              int32_t kv_splits);
 
-/* chunk_attention(q, cache) -> o.  Block-causal attention of the rotated
+/* chunk_attention(q, cache) -> o: causal attention of the new chunk over the
+ * KV cache (Causal-RoPE SP paper, sections 1 and 2(a): full spatio-temporal
+ * attention of a generated block over the cached keys of earlier blocks)
+ * restricted to the sink + rolling window of the StreamDiffusionV2 review,
+ * section 2.  Block-causal attention of the rotated
  * queries q_rot (qk_dtype) of frames t0[b] .. t0[b]+n_frames-1
  * (1 <= n_frames <= k*C) over the cached frames each query may see; o gets
  * the normalised output in the cache dtype, lse (nullable) the natural-log
@@ -274,6 +287,12 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
 size_t scv_rope_table_floats(const scv_cache* c, int32_t n_frames);
 scv_status scv_rope_tables(const scv_cache* c, const int64_t* t0, int32_t n_frames, float* out, size_t n_floats,
                            void* stream);
+
+/* The slot stamps (int64 [B][S_f + R]: the global frame each slot holds, -1
+ * when empty) copied to the host array out (n >= B * (S_f + R) entries).
+ * Synchronises the device first (every enqueued append has landed), so it is
+ * meant for checking, not for the streaming loop. */
+scv_status scv_debug_stamps(const scv_cache* c, int64_t* out, size_t n);
 
 /* Message describing the last non-OK status on this thread. */
 const char* scv_last_error(void);

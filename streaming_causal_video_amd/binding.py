@@ -95,6 +95,7 @@ _SIGNATURES = {
     ),
     "scv_rope_table_floats": (ctypes.c_size_t, [_VP, ctypes.c_int32]),
     "scv_rope_tables": (ctypes.c_int, [_VP, _I64P, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
+    "scv_debug_stamps": (ctypes.c_int, [_VP, _I64P, ctypes.c_size_t]),
     "scv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -343,9 +344,14 @@ class Cache:
                 raise ValueError(f"lse: need contiguous float32 {want}")
         if ws is None:
             # the schedule this request gets (from its t0), then exactly its
-            # workspace (None when it runs unsplit)
+            # workspace (None when it runs unsplit).  The workspace comes from
+            # torch's allocator on its current stream but is used on
+            # `stream`: record that use so the block is not handed out again
+            # before the kernels on `stream` are done with it.
             kv_splits = self.attention_splits(n_frames, kv_splits, t0=t0)
             ws = self.make_workspace(n_frames, kv_splits, t0=t0)
+            if ws is not None and stream is not None:
+                ws.record_stream(stream)
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(
             self.lib.scv_chunk_attention(self.handle, _ptr(q_rot), _t0_array(t0, self.cfg.batch), n_frames, _ptr(o),
@@ -374,6 +380,16 @@ class Cache:
             "h": out[nt : nt + nh].view(c.grid_h, dh // 2, 2),
             "w": out[nt + nh :].view(c.grid_w, dw // 2, 2),
         }
+
+    def debug_stamps(self):
+        """Slot stamps [B][n_slots] copied to the host by the library (the
+        call synchronises the device)."""
+        c = self.cfg
+        n = c.batch * int(self.layout.n_slots)
+        out = (ctypes.c_int64 * n)()
+        _check(self.lib.scv_debug_stamps(self.handle, out, n), "scv_debug_stamps")
+        return [[int(out[b * int(self.layout.n_slots) + s]) for s in range(int(self.layout.n_slots))]
+                for b in range(c.batch)]
 
     def views(self):
         """Typed views of the cache buffer, per the documented layout."""

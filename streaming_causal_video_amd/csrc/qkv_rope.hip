@@ -49,8 +49,12 @@ __device__ __forceinline__ void wait_vm() {
 // byte offset of 16-byte chunk c of row r in a slice (64-byte rows)
 __device__ __forceinline__ int slice_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
+// fp32 -> T (round to nearest even).  fp16 saturates: a value beyond the
+// largest finite fp16 is stored as +-65504 instead of +-inf, so rotated keys
+// stay finite and the attention over them stays defined.
 template <typename T>
 __device__ __forceinline__ uint16_t bits16(float x) {
+  if constexpr (std::is_same<T, _Float16>::value) x = __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f);
   return __builtin_bit_cast(uint16_t, static_cast<T>(x));
 }
 

@@ -98,9 +98,15 @@ __device__ __forceinline__ void unpack16(const uint4 u, float* x) {
 }
 
 // Two fp32 values rounded (to nearest even, native conversion) into the
-// 16-bit type T and packed.
+// 16-bit type T and packed.  fp16 saturates: a value beyond the largest
+// finite fp16 is stored as +-65504 instead of +-inf (rotated keys stay
+// finite, so attention over them stays defined).
 template <typename T>
 __device__ __forceinline__ uint32_t pack_x2(float lo, float hi) {
+  if constexpr (std::is_same<T, _Float16>::value) {
+    lo = __builtin_amdgcn_fmed3f(lo, -65504.f, 65504.f);
+    hi = __builtin_amdgcn_fmed3f(hi, -65504.f, 65504.f);
+  }
   const T a = static_cast<T>(lo);
   const T b = static_cast<T>(hi);
   return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);

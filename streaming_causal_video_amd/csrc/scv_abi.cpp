@@ -864,6 +864,21 @@ scv_status scv_rope_tables(const scv_cache* c, const int64_t* t0, int32_t n_fram
   }
 }
 
+scv_status scv_debug_stamps(const scv_cache* c, int64_t* out, size_t n) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if (!out) return fail(SCV_E_INVALID, "out is NULL");
+    const size_t need = size_t(c->g.B) * size_t(c->g.n_slots);
+    if (n < need) return fail(SCV_E_SHAPE, "out holds fewer than " + std::to_string(need) + " entries");
+    if ((s = hip_status(hipDeviceSynchronize(), "device synchronise")) != SCV_OK) return s;
+    return hip_status(hipMemcpy(out, c->base + c->lay.stamps_offset, need * sizeof(int64_t), hipMemcpyDeviceToHost),
+                      "stamps copy");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
 const char* scv_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -47,19 +47,30 @@ class StreamRunner:
         self.splits = self.cache.attention_splits(nq, kv_splits, t0=w.t0, ws_bytes=ws_bytes)
 
     def fill(self, stream=None):
-        """cache_init with the sink frames, then the window frames."""
+        """cache_init with the sink frames, then the window frames.  The
+        input temporaries are allocated on torch's current stream; when the
+        calls run on another `stream`, that use is recorded so that their
+        memory is not reused before those kernels have read it."""
         w = self.w
+
+        def used_on_stream(*ts):
+            if stream is not None:
+                for t in ts:
+                    t.record_stream(stream)
+
         if w.sink_frames > 0:
             zeros = [0] * w.batch
             sk = to_device(G.frames_tensor(w, G.TENSOR_K, zeros, w.sink_frames), w.dtype, self.device)
             sv = to_device(G.frames_tensor(w, G.TENSOR_V, zeros, w.sink_frames), w.dtype, self.device)
             self.cache.cache_init(sk, sv, stream=stream)
+            used_on_stream(sk, sv)
         else:
             self.cache.cache_init(stream=stream)
         for starts, n in fill_schedule(w):
             k = to_device(G.frames_tensor(w, G.TENSOR_K, starts, n), w.dtype, self.device)
             v = to_device(G.frames_tensor(w, G.TENSOR_V, starts, n), w.dtype, self.device)
             self.cache.rope3d_append(None, None, k, v, starts, n, stream=stream)
+            used_on_stream(k, v)
 
     def append(self, stream=None):
         self.cache.rope3d_append(self.q, self.q_rot, self.k, self.v, self.w.t0, self.n_frames, stream=stream)
