@@ -12,10 +12,11 @@
 // Kernels (MI355X / CDNA4, wave64):
 //  * chunk_attn_bf16_kernel (bf16 / fp16 operands, fp32 accumulation):
 //    8 waves = 256 query rows of one query chunk of one (stream, head[, key
-//    split]), 32 rows per wave, two waves per SIMD in ping-pong (one in its
-//    MFMA phase while the other runs its softmax); 64-key tiles move global
-//    -> LDS by direct 16-byte loads into a 4-stage ring.  Details above the
-//    kernel.
+//    split]), 32 rows per wave, two waves per SIMD; each wave runs its key
+//    loop software-pipelined in 32-key units, the softmax of one unit
+//    interleaved instruction by instruction with the MFMAs of its
+//    neighbours; 64-key tiles move global -> LDS by direct 16-byte loads
+//    into 4-stage K and V^T rings.  Details above the kernel.
 //  * chunk_attn_f32_kernel (fp32 end to end): 4 waves = 128 query rows,
 //    v_mfma_f32_32x32x2_f32, double-buffered LDS tiles staged through VGPRs.
 //  * attn_merge_kernel: combines the normalised fp32 partials of key splits
@@ -31,7 +32,9 @@
 //    max / row sum need one exchange with lane ^ 32, and P^T is directly the
 //    B operand of O^T += V^T P^T -- no LDS round trip for P.
 //  * V is stored transposed in the cache ([d][row]).
-//  * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
+//  * Online softmax in fp32 with exp2 (the bf16 kernel folds log2(e)/sqrt(d)
+//    into Q and the running reference into the S^T accumulator's start
+//    value; the fp32 kernel folds the scale into one FMA).
 //  * Query tiles never straddle query chunks; each workgroup derives the
 //    slots its chunk may see from the stamps once, skips invisible tiles and
 //    masks the hidden keys of partly visible ones.
@@ -46,6 +49,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -148,15 +152,15 @@ __device__ __forceinline__ bool tile_full(const Geometry& g, uint64_t slots, int
 //
 // Workgroup = 8 waves = 256 query rows of one (stream, head[, key split]);
 // each wave owns 32 query rows for the whole key loop, so a wave's S^T,
-// P^T, Q and O^T all stay in VGPRs.  Waves w and w + 4 share a SIMD and run
-// the same per-tile work in opposite order ("ping-pong"): waves 0-3 do
-// their MFMA phase (P V of the previous tile, then QK^T of this tile) and
-// then their softmax phase; waves 4-7 do the softmax of the previous tile
-// first.  While one wave of a SIMD is in its softmax (VALU), the other keeps
-// the matrix core busy.
+// P^T, Q and O^T all stay in VGPRs; waves w and w + 4 share a SIMD.  Each
+// wave walks the keys in 32-key units: step u issues the MFMAs of P V of
+// unit u-1 and of S^T of unit u+1, and between every two MFMAs the LDS read
+// of a later fragment and the exponential, sum and bf16 conversion of one
+// score of unit u -- so the matrix core and the VALU work side by side
+// within each wave instead of in alternating phases.
 // Tiles of 64 keys move global -> LDS through the 16-byte direct loads of
-// gfx950 (no VGPR staging) into a ring of 4 stages, two tiles ahead of use,
-// with one barrier per tile.  In LDS, K rows are permuted inside each 16-row
+// gfx950 (no VGPR staging) into K and V^T rings of 4 stages, two tiles
+// ahead of use, with one barrier per tile.  In LDS, K rows are permuted inside each 16-row
 // group (bits 2 and 3 of the row index swapped) so that the S^T accumulator
 // of lane half h holds, per 16-key group, exactly keys 8h..8h+7 of that
 // group: P^T then pairs with V^T read in natural key order (one 16-byte read
@@ -262,11 +266,11 @@ __device__ __forceinline__ WorkItem attn_work_item(const AttnArgs& a) {
 // LDS row r of a K tile holds key row kperm(r) of the tile.
 __device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-constexpr int kPPWaves = 8;                  // waves per workgroup (2 per SIMD)
-constexpr int kRowsBf16 = 32 * kPPWaves;     // 256 query rows per workgroup
+constexpr int kBf16Waves = 8;                  // waves per workgroup (2 per SIMD)
+constexpr int kRowsBf16 = 32 * kBf16Waves;     // 256 query rows per workgroup
 static_assert(kRowsBf16 == kAttnRowsBf16, "host and kernel agree on the query tile");
 constexpr int kStages = 4;                   // LDS tile ring
-constexpr int kDmaWaves = kPPWaves;          // every wave moves its share of a tile
+constexpr int kDmaWaves = kBf16Waves;          // every wave moves its share of a tile
 
 template <int D>
 struct Bf16Tile {
@@ -471,7 +475,6 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool lead = wave < 4;  // MFMA phase first
   const int hl = lane >> 5, l32 = lane & 31;
 
   // One segment: the visits [vis_lo, vis_hi) of key tiles [t_begin, t_end)
@@ -521,20 +524,33 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     const int r = (dw * T::V_DMA + i) * 8 + (lane >> 3);  // d row
     vvo[i] = uint32_t((lane >> 3) * vpitch + (((lane & 7) ^ T::vswz(r)) * 16));
   }
-  auto issue_tile = [&](int t, int stg) {
+  // LDS holds two rings of kStages stages: K tiles at [0, KRING) and V^T
+  // tiles at [KRING, 2*KRING).  Visit v's K tile goes to K stage v % 4 and
+  // its V^T tile to V stage v % 4.
+  constexpr int KRING = kStages * T::KBYTES;
+  // load i of this wave's share of the K (V^T) tile t into stage stg
+  auto issue_k1 = [&](int t, int stg, int i) __attribute__((always_inline)) {
     const int64_t r0 = int64_t(t) * kKeyTile;
-    const uint32_t dst = lds0 + uint32_t(stg * T::STAGE);
+    dma16(kbase + r0 * T::KROW, kvo[i], lds0 + uint32_t(stg * T::KBYTES + (dw * T::K_DMA + i) * 1024));
+  };
+  auto issue_v1 = [&](int t, int stg, int i) __attribute__((always_inline)) {
+    const int64_t r0 = int64_t(t) * kKeyTile;
+    const int n = dw * T::V_DMA + i;
+    dma16(vbase + int64_t(n * 8) * vpitch + r0 * 2, vvo[i], lds0 + uint32_t(KRING + stg * T::VBYTES + n * 1024));
+  };
+  auto issue_k = [&](int t, int stg) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < T::K_DMA; ++i)
-      dma16(kbase + r0 * T::KROW, kvo[i], dst + uint32_t((dw * T::K_DMA + i) * 1024));
+    for (int i = 0; i < T::K_DMA; ++i) issue_k1(t, stg, i);
+  };
+  auto issue_v = [&](int t, int stg) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < T::V_DMA; ++i) {
-      const int n = dw * T::V_DMA + i;
-      dma16(vbase + int64_t(n * 8) * vpitch + r0 * 2, vvo[i], dst + uint32_t(T::KBYTES + n * 1024));
-    }
+    for (int i = 0; i < T::V_DMA; ++i) issue_v1(t, stg, i);
   };
 
-  // Q^T operand: lane (l32, hl) holds q[qrow][16*kk + 8*hl .. +8].
+  // Q^T operand: lane (l32, hl) holds q[qrow][16*kk + 8*hl .. +8], scaled
+  // by log2(e)/sqrt(d) and rounded once more to the operand type, so that
+  // S^T comes out of the MFMAs in log2 units and the softmax needs no
+  // multiply per score.
   qk8 qf[KS];
   {
     const QKT* qp =
@@ -542,7 +558,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(qk8, u);
+      const qk8 x = __builtin_bit_cast(qk8, u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<QKT>(static_cast<float>(x[i]) * a.scale_log2);
     }
   }
   // Q has landed before any tile load is issued: a wait the compiler sees
@@ -550,156 +568,207 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   // Q inside the tile loop, where it would also wait for the prefetched tiles.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // loop-invariant LDS byte offsets of this lane's K and V^T fragments
+  // loop-invariant LDS byte offsets of this lane's K and V^T fragments inside
+  // stage 0 of their ring (a stage adds a constant)
   int koff[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) koff[kk] = l32 * T::KROW + (((2 * kk + hl) ^ T::kswz(l32)) * 16);
   int voff[4];
 #pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) voff[g4] = T::KBYTES + l32 * T::VROW + (((2 * g4 + hl) ^ T::vswz(l32)) * 16);
+  for (int g4 = 0; g4 < 4; ++g4) voff[g4] = KRING + l32 * T::VROW + (((2 * g4 + hl) ^ T::vswz(l32)) * 16);
 
   floatx16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = floatx16{};
+  // Softmax state in log2 units (scores are q.k * log2(e)/sqrt(d)): m_run
+  // is the row's reference (-inf until the row has seen a key), msc_run the
+  // reference the scores are taken against (0 while m_run is -inf).  The
+  // S^T MFMAs start from sbias = -msc_run, so the accumulator holds
+  // score - reference and the exponentials need no subtraction either.
   float m_run = -INFINITY, l_run = 0.f;
-  float msc_run = 0.f;                 // m_run * c (0 while m_run is -inf)
-  const float c = a.scale_log2;
+  float msc_run = 0.f;
+  floatx16 sbias = floatx16{};
   constexpr float kPBound = 1024.f;    // largest exponential kept (2^10)
 
-  floatx16 s[2];      // S^T of a tile: keys 32j .. 32j+31 (in kperm order) x this wave's 32 queries
-  bf16x8 p[2][2];     // P^T of a tile: [half j][16-key group gg]
-
-  // Fragment reads run kLookahead MFMAs ahead of their use (bounds the
-  // registers they hold while covering the LDS latency).
+  // The key loop runs in units of 32 keys (half a tile): unit u = 2v + h is
+  // half h of visit v.  Unit u's S^T (its 32 keys in kperm order x this
+  // wave's 32 queries) lives in sb[u % 2], its P^T in pb[u % 2] (16-key
+  // groups gg).
+  floatx16 sb[2];
+  bf16x8 pb[2][2];
+  constexpr int kPVH = 2 * DB;  // P V MFMAs per unit
+  constexpr int kQKH = KS;      // S^T MFMAs per unit
+  static_assert(kPVH % 4 == 0 && kQKH % 4 == 0, "fragment ring slots repeat per step");
+  // Fragment ring: the LDS operand of MFMA j of a step sits in ring[j % 4],
+  // read kLookahead MFMAs ahead; the reads run across step boundaries (the
+  // last MFMAs of a step read the first fragments of the next step, whose
+  // tiles were published at an earlier barrier), so no step starts with the
+  // matrix core waiting a full LDS latency.
   constexpr int kLookahead = 3;
-  auto interleave = [](int n_mfma) {
-    __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);  // LDS reads
-    for (int i = 0; i < n_mfma - kLookahead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  uint4 ring[4];
+
+  // One operand source of a step: P V of half h of the V^T tile in stage st
+  // (fragments n = gg * DB + db), or S^T of half h of the K tile in stage st
+  // (fragments kk).
+  struct Src {
+    bool pv;
+    int st, h;
+  };
+  auto read_frag = [&](const Src& src, int j) __attribute__((always_inline)) {
+    if (src.pv) {
+      const int db = j % DB, gg = j / DB;
+      return *reinterpret_cast<const uint4*>(smem + voff[2 * src.h + gg] + src.st * T::VBYTES + db * 32 * T::VROW);
     }
-    for (int i = 0; i < kLookahead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    return *reinterpret_cast<const uint4*>(smem + koff[j] + src.st * T::KBYTES + src.h * 32 * T::KROW);
   };
-  // S^T = K Q^T of the tile in stage st (the two 32-key halves alternate, so
-  // no MFMA waits on the one just issued)
-  auto qk_ops = [&](const char* st) {
-    s[0] = floatx16{};
-    s[1] = floatx16{};
+  // Masks the keys of half h of tile t that no query here may see.  Element
+  // i of a half's S^T in lane half hl is key kperm(8(i/4) + 4hl + i%4) of the
+  // half, that is key 16(a>>1) + 8hl + 4(a&1) + i%4 with a = i/4.
+  auto mask = [&](floatx16& s, int t, int h) __attribute__((always_inline)) {
+    const uint64_t km = tile_key_mask(g, slots, t) >> (32 * h + 8 * hl);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const qk8 kf = *reinterpret_cast<const qk8*>(st + koff[kk] + j * 32 * T::KROW);
-        s[j] = mfma_32x32x16(kf, qf[kk], s[j]);
-      }
-  };
-  // O^T += V^T P^T of the tile in stage st
-  // V^T fragment n (in P V order: j, gg, db) of the tile in stage st
-  auto vfrag = [&](const char* st, int n) {
-    const int db = n % DB, jg = n / DB;
-    return *reinterpret_cast<const bf16x8*>(st + voff[jg] + db * 32 * T::VROW);
-  };
-  // The first kLookahead fragments of the next P V are read at the end of
-  // the softmax phase, before the barrier that opens the MFMA phase (their
-  // tile was published a trip earlier), so the matrix core does not wait a
-  // full LDS latency at the start of every MFMA phase.
-  bf16x8 vpre[kLookahead];
-  auto pv_ops = [&](const char* st) {
-#pragma unroll
-    for (int n = 0; n < 4 * DB; ++n) {
-      const int j = n / (2 * DB), gg = (n / DB) % 2, db = n % DB;
-      const bf16x8 v = n < kLookahead ? vpre[n] : vfrag(st, n);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[j][gg], o[db], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      const int a4 = i / 4;
+      const int bit = 16 * (a4 >> 1) + 4 * (a4 & 1) + (i & 3);
+      s[i] = ((km >> bit) & 1) ? s[i] : -INFINITY;
     }
   };
-  auto qk = [&](const char* st) {
-    qk_ops(st);
-    interleave(2 * KS);
-  };
-  auto pv = [&](const char* st) {
-    pv_ops(st);
-    // the reads run kLookahead MFMAs ahead from the first MFMA on
-    for (int i = 0; i < 4 * DB - kLookahead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  // Exponentials 2^(s - shift), rounded to bf16 into p, with their fp32 sum
+  // over this lane's 16 keys (two chains).
+  auto exps = [&](const floatx16& s, float shift, bf16x8 (&p)[2], float& rs) __attribute__((always_inline)) {
+    float acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float f0 = fast_exp2(s[i] - shift);
+      const float f1 = fast_exp2(s[i + 1] - shift);
+      p[i / 8][i % 8] = static_cast<__bf16>(f0);
+      p[i / 8][i % 8 + 1] = static_cast<__bf16>(f1);
+      acc[0] += f0;
+      acc[1] += f1;
     }
-    for (int i = 0; i < kLookahead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    rs = acc[0] + acc[1];
   };
-  // Masks the keys of tile t that no query here may see.  Element i of s[j]
-  // in lane half hl is key 32j + kperm(8(i/4) + 4hl + i%4) of the tile, that
-  // is key 32j + 16(a>>1) + 8hl + 4(a&1) + i%4 with a = i/4.
-  auto mask = [&](int t) {
-    const uint64_t km = tile_key_mask(g, slots, t) >> (8 * hl);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int a4 = i / 4;
-        const int bit = 32 * j + 16 * (a4 >> 1) + 4 * (a4 & 1) + (i & 3);
-        s[j][i] = ((km >> bit) & 1) ? s[j][i] : -INFINITY;
-      }
-  };
-  // Exponentials of s against the reference offset msc, rounded to bf16 into
-  // p, with their fp32 sums over this lane's 32 keys (four chains).  The sums
-  // use plain adds: v_dot2c_f32_bf16 would stall while the SIMD's other wave
-  // streams MFMAs.
-  auto exps = [&](float msc, float* rs) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 16; i += 2)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float f0 = fast_exp2(__builtin_fmaf(s[j][i], c, -msc));
-        const float f1 = fast_exp2(__builtin_fmaf(s[j][i + 1], c, -msc));
-        p[j][i / 8][i % 8] = static_cast<__bf16>(f0);
-        p[j][i / 8][i % 8 + 1] = static_cast<__bf16>(f1);
-        acc[2 * j] += f0;
-        acc[2 * j + 1] += f1;
-      }
-    rs[0] = acc[0] + acc[1];
-    rs[1] = acc[2] + acc[3];
-  };
-  // Softmax of s into p.  The exponentials are taken against the running
-  // reference first; their row sums (needed anyway) show whether an element
-  // exceeds 2^10 or no reference exists yet.  Only then is the row max
-  // computed, the reference raised, O^T and l rescaled and the exponentials
-  // redone -- so elements never exceed 2^10 and the common path has no
-  // max reduction in front of the exponentials.
-  auto softmax = [&]() {
-    float rs[2];
-    exps(msc_run, rs);
-    if (__any((rs[0] + rs[1] > kPBound) || (m_run == -INFINITY))) {
+  // The exponentials were taken against the running reference; their row
+  // sums show whether an element exceeds 2^10 or no reference exists yet.
+  // Only then is the row max computed, the reference raised, O^T and l
+  // rescaled and the exponentials redone -- so elements never exceed 2^10
+  // and the common path has no max reduction in front of the exponentials.
+  // s_next (when NEXT) is S^T of the next unit, computed against the old
+  // reference: it moves with it.
+  auto finish_softmax = [&](floatx16& s, bf16x8 (&p)[2], float& rs, auto next_c,
+                            floatx16& s_next) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    if (__any((rs > kPBound) || (m_run == -INFINITY))) {
       // row max with v_max3_f32 issued directly (see vmax3); the fence makes
       // the wait states an MFMA result needs before such reads explicit
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]));
-      auto x = [&](int e) { return s[e / 16][e % 16]; };
-      float ch[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ch[q] = vmax3(x(8 * q), x(8 * q + 1), x(8 * q + 2));
-      const float e7 = vmax3(x(7), x(23), x(31));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ch[q] = vmax3(ch[q], x(8 * q + 3), x(8 * q + 4));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ch[q] = vmax3(ch[q], x(8 * q + 5), x(8 * q + 6));
-      const float mx = vmax3(vmax3(ch[0], ch[1], e7), vmax3(ch[2], ch[3], x(15)), m_run);
-      const float m_new = max_halves(mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s));
+      const float a0 = vmax3(s[0], s[1], s[2]), a1 = vmax3(s[3], s[4], s[5]);
+      const float a2 = vmax3(s[6], s[7], s[8]), a3 = vmax3(s[9], s[10], s[11]);
+      const float a4 = vmax3(s[12], s[13], s[14]), a5 = vmax3(s[15], a0, a1);
+      const float d = max_halves(vmax3(a2, a3, vmax3(a4, a5, -INFINITY)));  // row max of score - msc_run
+      const float m_new = fmaxf(m_run, msc_run + d);
+      const float msc_new = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      const float shift = msc_new - msc_run;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m_run = m_new;
-      msc_run = (m_run == -INFINITY) ? 0.f : m_run * c;
-      exps(msc_run, rs);
+      msc_run = msc_new;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sbias[i] = -msc_new;
+      if constexpr (NEXT) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s_next));
+        s_next -= shift;
+      }
+      exps(s, shift, p, rs);
     }
-    l_run += rs[0] + rs[1];
+    l_run += rs;
+  };
+  // One step of npv + nqk MFMAs (P V of the previous unit with p_prv from
+  // source pv_src, then S^T of the next unit into s_cur from source qk_src)
+  // with the softmax of this unit (s_prv -> p_new; sum in rs) spread over
+  // them, element by element; the reads of the next step's first fragments
+  // (source nx_src, when NX) close it.  Each MFMA, the LDS read kLookahead
+  // MFMAs ahead and its share of the softmax form one group that the
+  // compiler keeps in this order (sched_barrier), so the SIMD issues MFMA
+  // and VALU work side by side instead of in phases.
+  // SM: the step carries a softmax; OWN: it reads its own first fragments
+  // (the step before did not).
+  // extra(j) adds work to MFMA group j (the tile loads after a barrier).
+  auto step_ops = [&](auto npv_c, auto nqk_c, auto sm_c, auto own_c, auto nx_c, const Src& pv_src,
+                      const Src& qk_src, const Src& nx_src, const bf16x8 (&p_prv)[2], floatx16& s_cur,
+                      const floatx16& s_prv, bf16x8 (&p_new)[2], float& rs, auto&& extra) __attribute__((always_inline)) {
+    constexpr int NPV = decltype(npv_c)::value, NQK = decltype(nqk_c)::value;
+    constexpr bool SM = decltype(sm_c)::value, OWN = decltype(own_c)::value, NX = decltype(nx_c)::value;
+    constexpr int N = NPV + NQK;
+    static_assert(N > 0 && 16 % N == 0, "16 softmax elements per step");
+    constexpr int EPC = SM ? 16 / N : 0;  // softmax elements per MFMA group
+    float acc[2] = {0.f, 0.f};
+    float fprev = 0.f;
+    uint32_t pw[2][4];  // P^T of this unit, two bf16 per word
+    if constexpr (NQK > 0) s_cur = sbias;
+    // fragment j of this step, or of the next one for j >= N
+    auto fetch = [&](int j) __attribute__((always_inline)) {
+      if (j < NPV) {
+        ring[j % 4] = read_frag(pv_src, j);
+      } else if (j < N) {
+        ring[j % 4] = read_frag(qk_src, j - NPV);
+      } else if constexpr (NX) {
+        ring[j % 4] = read_frag(nx_src, j - N);
+      }
+    };
+    if constexpr (OWN) {
+#pragma unroll
+      for (int j = 0; j < kLookahead; ++j) fetch(j);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      if (j < NPV) {
+        const int gg = j / DB, db = j % DB;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ring[j % 4]), p_prv[gg], o[db], 0,
+                                                        0, 0);
+      } else {
+        s_cur = mfma_32x32x16(__builtin_bit_cast(qk8, ring[j % 4]), qf[j - NPV], s_cur);
+      }
+      fetch(j + kLookahead);
+      extra(j);
+#pragma unroll
+      for (int e = j * EPC; e < (j + 1) * EPC; ++e) {
+        const float f = fast_exp2(s_prv[e]);
+        acc[e & 1] += f;
+        // the empty volatile asm keeps the sum (and below the bf16 pair) in
+        // this group instead of letting them sink to the end of the step
+        asm volatile("" : "+v"(acc[e & 1]));
+        if (e & 1) {
+          const bf16x2 pr = {static_cast<__bf16>(fprev), static_cast<__bf16>(f)};
+          uint32_t w = __builtin_bit_cast(uint32_t, pr);
+          asm volatile("" : "+v"(w));
+          pw[e / 8][(e % 8) / 2] = w;
+        }
+        fprev = f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SM) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        p_new[gg] = __builtin_bit_cast(bf16x8, make_uint4(pw[gg][0], pw[gg][1], pw[gg][2], pw[gg][3]));
+    }
+    rs = acc[0] + acc[1];
   };
 
-  // The key loop over every tile with a visible key.  With tile i in LDS
-  // stage i % 4, each trip first publishes tile i (everyone's loads of it
-  // have landed) and starts the load of tile i + 2 into the stage of tile
-  // i - 2, which every wave finished in the previous trip.  Tiles that are
-  // only partly visible (slot padding, window edges, the row tail) have
-  // their hidden keys masked before the softmax.
+  // The key loop over every tile with a visible key, software-pipelined per
+  // wave in 32-key units: step u runs the MFMAs of P V of unit u-1 and of
+  // S^T of unit u+1 with the softmax of unit u interleaved between them
+  // (the SIMD's two waves run such steps side by side).  Visit v's tiles: K
+  // in K stage v % 4, V^T in V stage v % 4.  Barrier B_v (before the steps
+  // 2v-1 and 2v, which compute S^T of visit v) waits for K and V^T of visit
+  // v, loaded two barriers earlier, then starts the loads of V^T of visit
+  // v+2 and K of visit v+3 into the stages of visits v-2 and v-1, which
+  // every wave finished before B_v.  Tiles that are only partly visible
+  // (slot padding, window edges, the row tail) have their hidden keys
+  // masked before their softmax.
   RunWalk walk;
   walk.init(g, slots, t_begin, t_end);
   // every tile of the split fully visible (the steady state): no walk needed
@@ -733,10 +802,10 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   }
   // One key loop, instantiated twice: without any masking code when every
   // tile of the split is fully visible, and with masks otherwise.
-  auto key_loop = [&](auto masked_tag) {
+  auto key_loop = [&](auto masked_tag) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     int dense_t = t_begin - 1;
-    auto next_tile = [&](bool first, bool* full) {
+    auto next_tile = [&](bool first, bool* full) __attribute__((always_inline)) {
       if constexpr (!kMasked) {
         dense_t = first ? t_begin : dense_t + 1;
         *full = true;
@@ -745,77 +814,145 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         return walk.next(g, slots, first, full);
       }
     };
-    // Slots between barriers: the lead waves (0-3) run, for tile i, the MFMA
-    // phase M(i) (P V of tile i-1, S^T of tile i) in one slot and the softmax
-    // V(i) in the next; the other waves (4-7) pass one extra barrier first,
-    // so each runs M(i) while its SIMD partner runs V(i-1), and V(i) while
-    // the partner runs M(i+1).  Every wave loads its share of each tile:
-    // tile i+2 (into the stage of tile i-2, which both groups finished before
-    // the barrier that starts the wave's M(i)) as its V(i) starts; tile i+1
-    // is waited for before the barrier that ends the lead waves' V(i), which
-    // publishes it.  Every wave passes the same number of barriers.
-    bool f0 = true, f1 = true;                              // fully visible?
-    int tq0 = next_tile(true, &f0);                         // tile i
-    int tq1 = tq0 < t_end ? next_tile(false, &f1) : t_end;  // tile i + 1
-    if (tq0 < t_end) {
-      issue_tile(tq0, 0);
-      if (tq1 < t_end) {
-        issue_tile(tq1, 1);
-        wait_vm<T::DMA>();
-      } else {
-        wait_vm<0>();
+    auto next_or_end = [&](int prev, bool* full) __attribute__((always_inline)) {
+      if (prev >= t_end) {
+        *full = true;
+        return t_end;
       }
+      return next_tile(false, full);
+    };
+    auto mask_if = [&](floatx16& s, int t, bool full, int h) __attribute__((always_inline)) {
+      if constexpr (kMasked) {
+        if (!full) mask(s, t, h);
+      }
+    };
+    constexpr int KV = T::K_DMA + T::V_DMA;
+    // visit queue: tiles of visits v-1 .. v+3 (t_end: no such visit)
+    bool fp = true, f0 = true, f1 = true, f2 = true, f3 = true;
+    int tp = t_end;
+    int tv0 = next_tile(true, &f0);
+    if (tv0 >= t_end) return;
+    int tv1 = next_or_end(tv0, &f1);
+    int tv2 = next_or_end(tv1, &f2);
+    int tv3 = t_end;
+    // B_v: wait for K and V^T of visit v (loads after V^T of v: K of v+1,
+    // V^T of v+1 and K of v+2), barrier, then the loads of V^T of v+2 and K
+    // of v+3.  st = v % 4.
+    // Every barrier issues the same number of loads: a visit that does not
+    // exist loads the first tile again into its (free) stage, so the wait
+    // counts need no case analysis and the loads need no branch.
+    auto real = [&](int t) __attribute__((always_inline)) { return t < t_end ? t : t_begin; };
+    auto barrier_v = [&](int st) __attribute__((always_inline)) {
+      wait_vm<KV + T::K_DMA>();
       __syncthreads();
-      if (!lead) __syncthreads();
-      bool have_prev = false;  // tile i - 1 exists (its P V is pending)
-      int si = 0;              // stage of tile i
-      while (true) {
-        const bool cur = tq0 < t_end;
-        int tq2 = t_end;
-        bool f2 = true;
-        if (tq1 < t_end) tq2 = next_tile(false, &f2);
-        // M(i)
-        const char* st = smem + si * T::STAGE;
-        const char* stp = smem + ((si + kStages - 1) % kStages) * T::STAGE;
-        // the MFMA phase outranks the partner wave's softmax at issue
-        __builtin_amdgcn_s_setprio(1);
-        if (active && have_prev) pv(stp);
-        if (active && cur) qk(st);
-        __builtin_amdgcn_s_setprio(0);
-        // each wave's share of tile i+1 has landed before the barrier after
-        // which the first reader (a lead wave in M(i+1)) may start; a
-        // non-lead wave has issued nothing after it
-        if (!lead && tq1 < t_end) wait_vm<0>();
-        __syncthreads();
-        // V(i): the load of tile i+2 goes out here, in the VALU phase, so
-        // that its issue never holds up the MFMA phase
-        if (tq2 < t_end) issue_tile(tq2, (si + 2) % kStages);
-        if (cur && active) {
-          if constexpr (kMasked) {
-            if (!f0) mask(tq0);
-          }
-          softmax();
-          // the first fragments of this tile's P V, done in the next trip
-#pragma unroll
-          for (int n = 0; n < kLookahead; ++n) vpre[n] = vfrag(st, n);
-        }
-        if (lead && tq1 < t_end) {
-          if (tq2 < t_end)
-            wait_vm<T::DMA>();
-          else
-            wait_vm<0>();
-        }
-        __syncthreads();
-        if (!cur) break;
-        have_prev = true;
-        tq0 = tq1;
-        f0 = f1;
-        tq1 = tq2;
-        f1 = f2;
-        si = (si + 1) % kStages;
+      tv3 = next_or_end(tv2, &f3);
+      if (!active) {
+        issue_v(real(tv2), (st + 2) % 4);
+        issue_k(real(tv3), (st + 3) % 4);
       }
-      if (lead) __syncthreads();
+    };
+    // The same loads issued by a wave with steps: one per odd MFMA group of
+    // the step after the barrier, so that their issue overlaps the MFMAs.
+    auto loads_in_step = [&](int st) __attribute__((always_inline)) {
+      const int tv = real(tv2), tk = real(tv3), sv = (st + 2) & 3, sk = (st + 3) & 3;
+      return [=, &issue_v1, &issue_k1](int j) __attribute__((always_inline)) {
+        if (j & 1) {
+          const int i = j >> 1;
+          if (i < T::V_DMA)
+            issue_v1(tv, sv, i);
+          else if (i < T::V_DMA + T::K_DMA)
+            issue_k1(tk, sk, i - T::V_DMA);
+        }
+      };
+    };
+    auto no_extra = [](int) __attribute__((always_inline)) {};
+    auto advance = [&]() __attribute__((always_inline)) {
+      tp = tv0; fp = f0;
+      tv0 = tv1; f0 = f1;
+      tv1 = tv2; f1 = f2;
+      tv2 = tv3; f2 = f3;
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+    using C0 = std::integral_constant<int, 0>;
+    using CPV = std::integral_constant<int, kPVH>;
+    using CQK = std::integral_constant<int, kQKH>;
+
+    // ---- B_0 and the first step: S^T of units 0 and 1, softmax of unit 0 ----
+    issue_k(tv0, 0);
+    issue_v(tv0, 0);
+    issue_k(real(tv1), 1);
+    issue_v(real(tv1), 1);
+    issue_k(real(tv2), 2);
+    barrier_v(0);
+    if (active) {
+      // S^T of unit 0 alone (the fragment ring then holds the first
+      // fragments of the next step)
+      float rs;
+      step_ops(C0{}, CQK{}, No{}, Yes{}, Yes{}, Src{false, 0, 0}, Src{false, 0, 0}, Src{false, 0, 1}, pb[1], sb[0],
+               sb[1], pb[1], rs, loads_in_step(0));
+      mask_if(sb[0], tv0, f0, 0);
+      // S^T of unit 1 with the softmax of unit 0; then the first fragments
+      // of P V of unit 0
+      step_ops(C0{}, CQK{}, Yes{}, No{}, Yes{}, Src{false, 0, 0}, Src{false, 0, 1}, Src{true, 0, 0}, pb[1], sb[1],
+               sb[0], pb[0], rs, no_extra);
+      // the softmax of unit 0 ran against the reference that existed before
+      // it (none): finish it now
+      finish_softmax(sb[0], pb[0], rs, Yes{}, sb[1]);
     }
+    advance();
+    // visit v >= 1 (stage st = v % 4, a constant: the loop is unrolled four
+    // times so that every fragment read takes its stage as an immediate
+    // offset): steps 2v-1 and 2v
+    auto visit = [&](auto st_c) __attribute__((always_inline)) {
+      constexpr int st = decltype(st_c)::value, sp = (st + 3) & 3;  // sp: stage of visit v-1
+      // the fragment offsets pass through an empty asm each visit, so that
+      // offset + stage is formed at the read (as its immediate) instead of
+      // being hoisted out of the loop into a register per stage
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(koff[kk]));
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) asm volatile("" : "+v"(voff[g4]));
+      barrier_v(st);
+      if (active) {
+        float rs;
+        // step 2v-1: P V of unit 2v-2, S^T of unit 2v, softmax of unit 2v-1
+        mask_if(sb[1], tp, fp, 1);
+        step_ops(CPV{}, CQK{}, Yes{}, No{}, Yes{}, Src{true, sp, 0}, Src{false, st, 0}, Src{true, sp, 1}, pb[0],
+                 sb[0], sb[1], pb[1], rs, loads_in_step(st));
+        finish_softmax(sb[1], pb[1], rs, Yes{}, sb[0]);
+        // step 2v: P V of unit 2v-1, S^T of unit 2v+1, softmax of unit 2v
+        mask_if(sb[0], tv0, f0, 0);
+        step_ops(CPV{}, CQK{}, Yes{}, No{}, Yes{}, Src{true, sp, 1}, Src{false, st, 1}, Src{true, st, 0}, pb[1],
+                 sb[1], sb[0], pb[0], rs, no_extra);
+        finish_softmax(sb[0], pb[0], rs, Yes{}, sb[1]);
+      }
+      advance();
+    };
+    int st = 1;  // stage of the next visit
+    while (true) {
+      if (tv0 >= t_end) break;
+      visit(std::integral_constant<int, 1>{});
+      if (tv0 >= t_end) { st = 2; break; }
+      visit(std::integral_constant<int, 2>{});
+      if (tv0 >= t_end) { st = 3; break; }
+      visit(std::integral_constant<int, 3>{});
+      if (tv0 >= t_end) { st = 0; break; }
+      visit(std::integral_constant<int, 0>{});
+    }
+    // after the last visit v = n-1 (stage (st + 3) % 4): the softmax of unit
+    // 2n-1 with P V of unit 2n-2, then P V of unit 2n-1
+    if (active) {
+      const int sl = (st + 3) & 3;
+      float rs;
+      mask_if(sb[1], tp, fp, 1);
+      step_ops(CPV{}, C0{}, Yes{}, No{}, Yes{}, Src{true, sl, 0}, Src{false, 0, 0}, Src{true, sl, 1}, pb[0], sb[0],
+               sb[1], pb[1], rs, no_extra);
+      finish_softmax(sb[1], pb[1], rs, No{}, sb[0]);
+      step_ops(CPV{}, C0{}, No{}, No{}, No{}, Src{true, sl, 1}, Src{false, 0, 0}, Src{false, 0, 0}, pb[1], sb[0],
+               sb[1], pb[0], rs, no_extra);
+    }
+    wait_vm<0>();  // the loads of visits past the end have landed too
   };
   if (dense)
     key_loop(std::false_type{});
@@ -824,7 +961,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_v = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+  const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   if (!qvalid) return;
   if (!partial) {
     __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t(b) * a.Nq + qrow) * g.H + head) * D;
