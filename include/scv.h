@@ -280,6 +280,23 @@ size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* 
 scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
                                float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream);
 
+/* chunk_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and schedule choice as scv_chunk_attention, with the
+ * workspace taken from a static device array of SCV_SCRATCH_BYTES bytes that
+ * the library holds on every GPU it runs on until the process ends.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ * kv_splits = 0 chooses among the schedules whose workspace fits the
+ * scratch; a forced schedule (kv_splits > 0 or -1) that needs more fails
+ * with SCV_E_WORKSPACE and nothing enqueued.  Every call on a GPU shares
+ * that GPU's scratch: calls whose executions overlap on one GPU (several
+ * streams, several threads) race and must be serialised by the caller.
+ * Nothing in the scratch needs to start at zero: a call writes every part
+ * of it that it reads. */
+#define SCV_SCRATCH_BYTES ((size_t)128 << 20)
+scv_status scv_chunk_attention_scratch(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames,
+                                       void* o, float* lse, int32_t kv_splits, void* stream);
+
 /* The fp32 cos/sin tables the kernels use for this request, written to the
  * device buffer out (fp32, n_floats >= scv_rope_table_floats(c, n_frames)):
  * [B][n_frames][d_t/2][2] for time, then [grid_h][d_h/2][2] for rows, then

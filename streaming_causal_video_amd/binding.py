@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libscv.so")
 
 SCV_FP32, SCV_BF16, SCV_FP16 = 0, 1, 2
+SCRATCH_BYTES = 128 << 20  # SCV_SCRATCH_BYTES: the static workspace of scv_chunk_attention_scratch
 _DTYPE_CODES = {"fp32": SCV_FP32, "bf16": SCV_BF16, "fp16": SCV_FP16}
 STATUS_NAMES = {
     0: "SCV_OK",
@@ -92,6 +93,10 @@ _SIGNATURES = {
     "scv_chunk_attention": (
         ctypes.c_int,
         [_VP, _VP, _I64P, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _VP, ctypes.c_size_t, _VP],
+    ),
+    "scv_chunk_attention_scratch": (
+        ctypes.c_int,
+        [_VP, _VP, _I64P, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _VP],
     ),
     "scv_rope_table_floats": (ctypes.c_size_t, [_VP, ctypes.c_int32]),
     "scv_rope_tables": (ctypes.c_int, [_VP, _I64P, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
@@ -357,6 +362,23 @@ class Cache:
             self.lib.scv_chunk_attention(self.handle, _ptr(q_rot), _t0_array(t0, self.cfg.batch), n_frames, _ptr(o),
                                          _ptr(lse), kv_splits, _ptr(ws), ws_bytes, _stream(stream)),
             "scv_chunk_attention",
+        )
+
+    def chunk_attention_scratch(self, q_rot, t0, n_frames, o, lse=None, kv_splits=0, stream=None):
+        """chunk_attention with the library's static scratch as workspace:
+        allocates nothing (calls overlapping on one GPU race)."""
+        import torch
+
+        self._tok(q_rot, n_frames, "q_rot", rotated=True)
+        self._tok(o, n_frames, "o")
+        if lse is not None:
+            want = (self.cfg.batch, self.cfg.heads, n_frames * self.P)
+            if tuple(lse.shape) != want or lse.dtype != torch.float32 or not lse.is_contiguous():
+                raise ValueError(f"lse: need contiguous float32 {want}")
+        _check(
+            self.lib.scv_chunk_attention_scratch(self.handle, _ptr(q_rot), _t0_array(t0, self.cfg.batch), n_frames,
+                                                 _ptr(o), _ptr(lse), kv_splits, _stream(stream)),
+            "scv_chunk_attention_scratch",
         )
 
     def rope_tables(self, t0, n_frames, stream=None):

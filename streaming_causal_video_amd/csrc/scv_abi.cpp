@@ -734,9 +734,25 @@ size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* 
   }
 }
 
-scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
-                               float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream) {
-  try {
+}  // extern "C"
+
+// The library's own workspace for scv_chunk_attention_scratch: device memory
+// that exists on every GPU the library runs on from module load to process
+// end, so that the call allocates nothing.  Host code never passes this name
+// to a kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SCV_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = SCV_SCRATCH_BYTES;
+
+// chunk_attention with the workspace ws of ws_bytes bytes (the caller's, or
+// the library's static scratch when from_scratch).
+scv_status chunk_attention_impl(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
+                                float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream,
+                                bool from_scratch) {
+  {
     scv_status s;
     if ((s = check_cache(c)) != SCV_OK) return s;
     if ((s = check_ptr(q_rot, "q_rot", true)) != SCV_OK) return s;
@@ -755,6 +771,10 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
       plan = lean_plan(c, n_frames, lean_units);
     }
     const size_t need = splits < 0 ? lean_workspace_bytes(c, plan.ctas) : workspace_bytes(c, n_frames, splits);
+    if (need > 0 && from_scratch && need > ws_bytes)
+      return fail(SCV_E_WORKSPACE, "this request's schedule needs " + std::to_string(need) +
+                                       " bytes of workspace; the library's static scratch holds " +
+                                       std::to_string(ws_bytes) + " (use scv_chunk_attention with a workspace)");
     if (need > 0) {
       if (!ws) return fail(SCV_E_WORKSPACE, "workspace is NULL; need " + std::to_string(need) + " bytes");
       if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SCV_E_ALIGN, "workspace must be 256-byte aligned");
@@ -829,6 +849,53 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
       if ((s = hip_status(scv::launch_attn_merge(m, st), "attn_merge launch")) != SCV_OK) return s;
     }
     return SCV_OK;
+  }
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device; nullptr (message in g_last_error) when the lookup fails.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* ptr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    g_last_error = "no current HIP device (or more than 64 devices)";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames, void* o,
+                               float* lse, int32_t kv_splits, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    return chunk_attention_impl(c, q_rot, t0, n_frames, o, lse, kv_splits, ws, ws_bytes, stream, false);
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
+scv_status scv_chunk_attention_scratch(const scv_cache* c, const void* q_rot, const int64_t* t0, int32_t n_frames,
+                                       void* o, float* lse, int32_t kv_splits, void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    void* ws = scratch_on_current_device();
+    if (!ws) return SCV_E_HIP;
+    return chunk_attention_impl(c, q_rot, t0, n_frames, o, lse, kv_splits, ws, kScratchBytes, stream, true);
   } catch (...) {
     return fail(SCV_E_INVALID, "internal error");
   }
