@@ -32,9 +32,10 @@
 //    max / row sum need one exchange with lane ^ 32, and P^T is directly the
 //    B operand of O^T += V^T P^T -- no LDS round trip for P.
 //  * V is stored transposed in the cache ([d][row]).
-//  * Online softmax in fp32 with exp2 (the bf16 kernel folds log2(e)/sqrt(d)
-//    into Q and the running reference into the S^T accumulator's start
-//    value; the fp32 kernel folds the scale into one FMA).
+//  * Online softmax in fp32 with exp2 (the fp32 kernel folds scale * log2 e
+//    into one FMA; the bf16 kernel folds it into Q and the running
+//    reference into the S^T accumulator's start value, so a score costs one
+//    exponential and no other arithmetic before it).
 //  * Query tiles never straddle query chunks; each workgroup derives the
 //    slots its chunk may see from the stamps once, skips invisible tiles and
 //    masks the hidden keys of partly visible ones.
@@ -665,7 +666,8 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       const float a0 = vmax3(s[0], s[1], s[2]), a1 = vmax3(s[3], s[4], s[5]);
       const float a2 = vmax3(s[6], s[7], s[8]), a3 = vmax3(s[9], s[10], s[11]);
       const float a4 = vmax3(s[12], s[13], s[14]), a5 = vmax3(s[15], a0, a1);
-      const float d = max_halves(vmax3(a2, a3, vmax3(a4, a5, -INFINITY)));  // row max of score - msc_run
+      // row max of (score - msc_run), in log2 units
+      const float d = max_halves(vmax3(a2, a3, vmax3(a4, a5, -INFINITY)));
       const float m_new = fmaxf(m_run, msc_run + d);
       const float msc_new = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);

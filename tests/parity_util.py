@@ -6,6 +6,7 @@ on the same seeded inputs, then evaluates attention in fp64.
 """
 from __future__ import annotations
 
+import json
 import sys
 
 import mpmath
@@ -77,23 +78,37 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
-def check_values(name, got, ref, dtype, per_axis0=False):
-    """fp32: max |err| <= 1e-4; bf16: relative L2 <= 1e-2 (overall and, with
-    per_axis0, per stream).  Returns the error figure."""
+def record(**fields):
+    """One machine-readable result line (collected into the results table of
+    the design notes from a run with output shown)."""
+    say("PARITY " + json.dumps(fields, sort_keys=True))
+
+
+def check_values(name, got, ref, dtype, per_axis0=False, tag=None):
+    """fp32: max |err| <= 1e-4; bf16: relative L2 <= 1e-2 overall and, with
+    per_axis0, per stream; for [B, M, H, d] outputs the worst (stream, head)
+    relative L2 is reported too.  Returns the error figure; with tag, records
+    the figures."""
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     if dtype == "fp32":
         err = float(np.max(np.abs(got - ref))) if got.size else 0.0
         say(f"  {name}: max-abs {err:.3e}")
+        if tag:
+            record(case=tag, what=name, metric="max-abs", value=err)
         assert err <= FP32_MAX_ABS, (name, err)
         return err
     err = rel_l2(got, ref)
-    say(f"  {name}: rel-L2 {err:.3e}")
+    per_head = None
+    if got.ndim == 4:
+        per_head = max(rel_l2(got[b, :, h], ref[b, :, h]) for b in range(got.shape[0]) for h in range(got.shape[2]))
+    per_stream = max(rel_l2(got[b], ref[b]) for b in range(got.shape[0])) if per_axis0 else None
+    say(f"  {name}: rel-L2 {err:.3e}" + (f", worst (stream, head) {per_head:.3e}" if per_head is not None else ""))
+    if tag:
+        record(case=tag, what=name, metric="rel-L2", value=err, worst_stream_head=per_head, worst_stream=per_stream)
     assert err <= BF16_REL_L2, (name, err)
     if per_axis0:
-        for b in range(got.shape[0]):
-            eb = rel_l2(got[b], ref[b])
-            assert eb <= BF16_REL_L2, (name, b, eb)
+        assert per_stream <= BF16_REL_L2, (name, per_stream)
     return err
 
 
