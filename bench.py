@@ -36,10 +36,10 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md (grid schedule, one launch)
-    "wan1.3b-480p": {"source": "f1a45a201f763f52", "kv_splits": 1, "bytes_per_launch": 344382362},
+    "wan1.3b-480p": {"source": "62887ad862daf2f8", "kv_splits": 1, "bytes_per_launch": 391155712},
     # profiles/chunk_attn_wan13b_720p_balanced.md (balanced schedule: the
     # attention launch and its merge launch, as timed together)
-    "wan1.3b-720p": {"source": "f1a45a201f763f52", "kv_splits": -1, "bytes_per_launch": 3355016806},
+    "wan1.3b-720p": {"source": "62887ad862daf2f8", "kv_splits": -1, "bytes_per_launch": 3590070784},
 }
 KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
 
@@ -90,50 +90,179 @@ def visible_pairs(w, stamps):
     return total
 
 
-def cpu_baseline(w, target_s=12.0):
-    """The fp64 oracle (as it stands) on a sample of query rows of the same
-    workload; returns TFLOP/s of its attention and what the sample was."""
-    import numpy as np
-
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from parity_util import oracle_replay
-
+def _host_info():
+    """Host CPU model, logical CPU count and the BLAS thread count numpy uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    log("cpu_baseline: oracle replay (fill) ...")
-    oc, q_rot = oracle_replay(w)
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "blas_threads": blas}
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The fp64 oracle (as it stands) on the same workload, timed on the host
+    cores: its rope3d_append of the query chunk (whole chunk) plus its chunk
+    attention on a random sample of query rows (all heads, all visible keys)
+    scaled to every row; each part the median of 3 runs.  Returns TFLOP/s of
+    that step (attention FLOPs per step time) and latent frames/s."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_util import oracle_fill
+
+    from streaming_causal_video_amd import datagen as G
+
+    info = _host_info()
+    log("cpu_baseline: oracle fill (untimed) ...")
+    oc = oracle_fill(w)
+    nq = w.query_frames
+    q = G.frames_tensor(w, G.TENSOR_Q, w.t0, nq)
+    k = G.frames_tensor(w, G.TENSOR_K, w.t0, nq)
+    v = G.frames_tensor(w, G.TENSOR_V, w.t0, nq)
+
+    def median3(fn):
+        ts = []
+        for _ in range(3):
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+        return sorted(ts)[1]
+
+    holder = {}
+    t_ra = median3(lambda: holder.__setitem__("q_rot", oc.rope3d_append(q, k, v, w.t0, nq)))
+    q_rot = holder["q_rot"]
     rng = np.random.default_rng(0)
-    nq = w.query_rows
-    n = 64
-    spent = 0.0
-    flops = 0
-    pairs_per_row = None
-    while spent < target_s and n <= nq:
-        rows = np.sort(rng.choice(nq, size=n, replace=False))
-        t = time.perf_counter()
-        oc.chunk_attention(q_rot, w.t0, w.query_frames, rows=rows)
-        dt = time.perf_counter() - t
-        if pairs_per_row is None:
-            # visible keys per row (same for every row of a one-chunk query)
-            keys = sum(len(oc.visible_slots(b, w.t0[b])) for b in range(w.batch)) * w.tokens_per_frame
-            pairs_per_row = keys
-        spent += dt
-        flops += 4 * w.head_dim * w.heads * n * pairs_per_row
-        n *= 2
-    rate = flops / spent / 1e12
+    # calibrate the row sample so that one attention run takes ~budget/6
+    t = time.perf_counter()
+    oc.chunk_attention(q_rot, w.t0, nq, rows=np.sort(rng.choice(w.query_rows, 32, replace=False)))
+    per_row = (time.perf_counter() - t) / 32
+    n = int(min(w.query_rows, max(32, (budget_s / 6.0 - 3 * t_ra / 6.0) / max(per_row, 1e-6))))
+    rows = np.sort(rng.choice(w.query_rows, n, replace=False))
+    t_att = median3(lambda: oc.chunk_attention(q_rot, w.t0, nq, rows=rows)) * (w.query_rows / n)
+    keys = sum(len(oc.visible_slots(b, w.t0[b])) for b in range(w.batch)) * w.tokens_per_frame
+    flops = 4 * w.head_dim * w.heads * w.query_rows * keys
+    step_s = t_ra + t_att
     return {
-        "value": rate,
+        "value": flops / step_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": cores,
+        "cores": info["blas_threads"] or info["cpu_count"],
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle chunk attention on {flops / (4 * w.head_dim * w.heads * pairs_per_row):.0f} "
-        f"query rows (random, all {w.heads} heads, all visible keys) of {w.name}; {spent:.1f} s of CPU time; "
-        f"cache filled by the oracle beforehand (untimed)",
+        "sample": f"fp64 numpy oracle on {w.name}: rope3d_append of the whole query chunk ({t_ra:.2f} s) plus chunk "
+        f"attention of {n} random query rows (all {w.heads} heads, all visible keys) scaled to {w.query_rows} rows "
+        f"({t_att:.1f} s); each part the median of 3 runs; cache filled by the oracle beforehand (untimed)",
+        "latent_frames_per_s": w.batch * w.query_frames / step_s,
+        "step_s": step_s,
+        **info,
     }
+
+
+SAMPLER = r"""
+import json, subprocess, sys, time
+out, stop, exe = sys.argv[1], sys.argv[2], sys.argv[3]
+t_end = time.time() + 600
+with open(out, "w") as f:
+    while time.time() < t_end:
+        try:
+            open(stop).close()
+            break
+        except OSError:
+            pass
+        t = time.time()
+        try:
+            p = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=20)
+            f.write(json.dumps({"t0": t, "t1": time.time(), "out": p.stdout}) + "\n")
+            f.flush()
+        except Exception:
+            pass
+        time.sleep(0.1)
+"""
+
+
+def start_clock_sampler():
+    """Starts, before this process touches the GPU, a child process that
+    polls amd-smi's per-XCD shader clock with wall-clock timestamps (the
+    bench itself never starts a program after it has initialised the GPU).
+    Returns a handle for read_clock_samples, or None without amd-smi."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if exe is None:
+        return None
+    d = tempfile.mkdtemp(prefix="scv_clk_")
+    out, stop = os.path.join(d, "samples.jsonl"), os.path.join(d, "stop")
+    proc = subprocess.Popen([sys.executable, "-c", SAMPLER, out, stop, exe], stdout=subprocess.DEVNULL,
+                            stderr=subprocess.DEVNULL)
+    import atexit
+
+    atexit.register(lambda: open(stop, "w").close())  # the sampler ends with the bench, whatever happens
+    return {"proc": proc, "out": out, "stop": stop}
+
+
+def read_clock_samples(h, t_lo, t_hi):
+    """Stops the sampler; mean per-XCD shader clock (MHz) over the samples
+    taken entirely inside the wall-clock window [t_lo, t_hi]."""
+    if h is None:
+        return None
+    open(h["stop"], "w").close()
+    try:
+        h["proc"].wait(timeout=30)
+    except Exception:  # pragma: no cover
+        h["proc"].kill()
+    clocks, n = [], 0
+    try:
+        lines = open(h["out"]).read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        rec = json.loads(line)
+        if rec["t0"] < t_lo or rec["t1"] > t_hi:
+            continue
+        try:
+            data = json.loads(rec["out"])
+        except ValueError:
+            continue
+        n += 1
+        for gpu in data.get("gpu_data", []):
+            for key, val in gpu.get("clock", {}).items():
+                if key.lower().startswith("gfx_") and isinstance(val, dict):
+                    c = val.get("clk", {})
+                    c = c.get("value") if isinstance(c, dict) else c
+                    try:
+                        clocks.append(float(c))
+                    except (TypeError, ValueError):
+                        pass
+    if not clocks:
+        return None
+    return {"mhz_mean": sum(clocks) / len(clocks), "mhz_min": min(clocks), "mhz_max": max(clocks), "samples": n,
+            "source": "amd-smi metric --clock (per XCD), polled by a helper process while attention launches ran "
+            "back to back for 3 s after the timed steps"}
+
+
+def load_window(r, seconds=3.0):
+    """Back-to-back attention launches for `seconds` (wall clock); returns
+    the window."""
+    import torch
+
+    t_lo = time.time()
+    while time.time() < t_lo + seconds:
+        for _ in range(100):
+            r.attend()
+        torch.cuda.synchronize()
+    return t_lo + 0.5, time.time()
 
 
 def cold_step_ms(r, reps=5, flush_bytes=512 << 20):
@@ -277,6 +406,7 @@ def main():
     ap.add_argument("--workload", default="wan1.3b-480p")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi shader-clock sampling")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     ap.add_argument("--ablations", action="store_true",
@@ -291,6 +421,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+
+    # before anything touches the GPU
+    clock_sampler = None if (args.ablations or args.no_clock) else start_clock_sampler()
 
     import torch
 
@@ -391,6 +524,7 @@ def main():
     # the projection first: the refreshes move time positions below t0
     out["next_rows"] = {"qkv_rope_append": time_qkv(r, w)} if w.dtype == "bf16" else {}
     out["next_rows"].update(time_refresh_and_sink(r, w))
+    out["sclk_under_load"] = read_clock_samples(clock_sampler, *load_window(r)) if clock_sampler else None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
