@@ -22,8 +22,15 @@
 // For q and k the MFMA computes C^T (features as rows) so that each lane
 // holds the dim pairs (2j, 2j+1) of one token, which RoPE rotates in
 // registers; for v it computes C (tokens as rows) so that each lane holds 4
-// consecutive tokens of one feature: one 8-byte store into the transposed
-// value cache.
+// consecutive tokens of one feature.
+// Epilogue: once every wave is done with the ring, it holds the RoPE
+// tables (time pairs of the tile's frames computed from fp64 angles, copies
+// of the height and width tables), so that every cos/sin comes from LDS, and
+// one staging area per wave: a wave rotates and rounds a 32-token block,
+// writes it into its area and reads it back as 16-byte pieces of whole rows
+// (a token's D features for q and k, 8 consecutive tokens of one feature for
+// the transposed value cache), so that the stores leave in contiguous
+// 64-byte or longer runs instead of 8-byte pieces scattered over 32 rows.
 #include <type_traits>
 
 #include "scv_internal.h"
@@ -36,10 +43,17 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kQK = 32;        // reduction depth of one LDS stage
 constexpr int kQTokGroups = 4; // waves per feature block
-constexpr int kTabFrames = 8;  // time-axis cos/sin of up to 8 frames in LDS
 
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(voff), "s"(base) : "m0", "memory");
+}
+// a pointer every lane holds the same value of, in scalar registers (the
+// direct-to-LDS loads take their base address from an SGPR pair)
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -52,6 +66,13 @@ __device__ __forceinline__ int slice_off(int r, int c) { return r * 64 + ((c ^ (
 // fp32 -> T (round to nearest even).  fp16 saturates: a value beyond the
 // largest finite fp16 is stored as +-65504 instead of +-inf, so rotated keys
 // stay finite and the attention over them stays defined.
+// cos/sin of a time pair whose frame is not in the LDS table (a tile
+// spanning more frames than the table holds); out of line so that the
+// compiler never evaluates it speculatively on the common path
+__device__ __attribute__((noinline)) float2 rope_cos_sin_slow(int64_t pos, double omega) {
+  return rope_cos_sin(pos, omega);
+}
+
 template <typename T>
 __device__ __forceinline__ uint16_t bits16(float x) {
   if constexpr (std::is_same<T, _Float16>::value) x = __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f);
@@ -82,7 +103,6 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   constexpr int DB = D / 32;
   static_assert(X_DMA >= 1 && W_DMA >= 1, "tile sizes");
   __shared__ __attribute__((aligned(1024))) char smem[kQStages * STAGE];
-  __shared__ float2 tab_t[kTabFrames * kMaxAxisPairs];
 
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -115,15 +135,6 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const int f_lo = m0 / g.P;
   const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
 
-  // time-axis cos/sin of the frames this tile starts in (fp64 angles)
-  {
-    const int nf = min(kTabFrames, a.n_frames - f_lo);
-    for (int i = tid; i < nf * pt; i += kThreads) {
-      const int fi = i / pt, j = i - fi * pt;
-      tab_t[fi * kMaxAxisPairs + j] = rope_cos_sin(a.t0[b] + f_lo + fi - a.pos_off[b], a.omega_t[j]);
-    }
-  }
-
   // ---- global -> LDS slices (source offsets are loop invariant) ----
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
   const char* xbase = static_cast<const char*>(a.x) + int64_t(b) * Ntok * Dm * 2;
@@ -146,9 +157,9 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
     const uint32_t dst = lds0 + uint32_t(stg * STAGE);
     const int64_t k0 = int64_t(kt) * kQK * 2;
 #pragma unroll
-    for (int j = 0; j < X_DMA; ++j) dma16(xbase + k0, xo[j], dst + uint32_t((wave * X_DMA + j) * 1024));
+    for (int j = 0; j < X_DMA; ++j) dma16(uniform_ptr(xbase + k0), xo[j], dst + uint32_t((wave * X_DMA + j) * 1024));
 #pragma unroll
-    for (int j = 0; j < W_DMA; ++j) dma16(wbase + k0, wo[j], dst + uint32_t(XB + (wave * W_DMA + j) * 1024));
+    for (int j = 0; j < W_DMA; ++j) dma16(uniform_ptr(wbase + k0), wo[j], dst + uint32_t(XB + (wave * W_DMA + j) * 1024));
   };
 
   floatx16_t acc[DB * TB];
@@ -248,81 +259,152 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
     return gf < g.S_f ? gf : g.S_f + gf % g.R;
   };
 
-  if (sel < 2) {
+  if (sel < 2)
     gemm(std::true_type{});
-    if (!fb_valid) return;  // after the last barrier
-    // lane: token 32TB*wq + 32tb + l32 of the tile; dims 32db + 8e + 4hl + 0..3
+  else
+    gemm(std::false_type{});
+
+  // ---- after the K loop the ring holds, from its start, the RoPE tables
+  // (cos/sin of the time pairs of the frames this tile spans, computed from
+  // fp64 angles, then copies of the height and width tables) and, at its
+  // end, one staging area per wave through which the outputs leave in whole
+  // 16-byte pieces of contiguous rows ----
+  constexpr int kRing = kQStages * STAGE;
+  constexpr int kStageOut = 32 * D * 2;             // one 32-token x D block
+  constexpr int kOutBase = kRing - kQWaves * kStageOut;
+  static_assert(kOutBase >= 16384, "room for the tables");
+  float2* tab = reinterpret_cast<float2*>(smem);
+  char* outst = smem + kOutBase + wave * kStageOut;  // this wave's staging area
+  const int dh2 = g.dh / 2, dw2 = g.dw / 2;
+  const int hw_n = g.grid_h * dh2 + g.grid_w * dw2;
+  const int f_hi = (min(m0 + kQM, Ntok) - 1) / g.P;
+  constexpr int kTabCap = kOutBase / int(sizeof(float2));
+  const bool hw_lds = hw_n <= kTabCap / 2;  // else read from global memory
+  const int nf_tab = min(f_hi - f_lo + 1, (kTabCap - (hw_lds ? hw_n : 0)) / max(pt, 1));
+  const int h_base = nf_tab * pt, w_base = h_base + g.grid_h * dh2;
+  __syncthreads();  // every wave is done with the ring
+  for (int i = tid; i < nf_tab * pt; i += kThreads) {
+    const int fi = i / pt, j = i - fi * pt;
+    tab[i] = rope_cos_sin(t0 + f_lo + fi - a.pos_off[b], a.omega_t[j]);
+  }
+  if (hw_lds) {
+    for (int i = tid; i < g.grid_h * dh2; i += kThreads) tab[h_base + i] = a.tab_h[i];
+    for (int i = tid; i < g.grid_w * dw2; i += kThreads) tab[w_base + i] = a.tab_w[i];
+  }
+  __syncthreads();
+  if (!fb_valid) return;
+  // frame of token t and its ring row (slot * slot_rows + position)
+  auto ring_row = [&](int t) -> int64_t {
+    const int f = t / g.P;
+    return slot_of(f) * g.slot_rows + (t - f * g.P);
+  };
+
+  if (sel < 2) {
+    // lane: token 32TB*wq + 32tb + l32 of the tile; dims 32db + 8e + 4hl + 0..3,
+    // that is pairs j = 16db + 4e + 2hl + 0..1.  Staging: [32 tokens][D],
+    // 16-byte chunk c of row r at c ^ (r % kChunks).
+    constexpr int kChunks = D / 8;
+    QT* const out_base = sel == 0 ? static_cast<QT*>(a.q_out) + (int64_t(b) * Ntok * g.H + head) * D
+                                  : static_cast<QT*>(a.cache_k) + (int64_t(b) * g.H + head) * g.rows_pad * D;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int t = m0 + 32 * TB * wq + 32 * tb + l32;
-      if (t >= Ntok) continue;
-      const int f = t / g.P, p = t - f * g.P;
-      const int yy = p / g.grid_w, xx = p - yy * g.grid_w;
-      const int fi = f - f_lo;
-      QT* dst;
-      if (sel == 0)
-        dst = static_cast<QT*>(a.q_out) + ((int64_t(b) * Ntok + t) * g.H + head) * D;
-      else
-        dst = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + slot_of(f) * g.slot_rows + p) * D;
+      const int tile0 = m0 + 32 * TB * wq + 32 * tb;  // first token of this block
+      {
+        const int t = min(tile0 + l32, Ntok - 1);  // rows past the last token are computed but not stored
+        const int f = t / g.P, p = t - f * g.P;
+        const int yy = p / g.grid_w, xx = p - yy * g.grid_w;
+        const int fi = f - f_lo;
+        // entry bases such that pair j's entry is base + j
+        const int tbase = fi * pt;
+        const int hbase = h_base + yy * dh2 - pt, wbase = w_base + xx * dw2 - pth;
+        const bool t_in_tab = fi < nf_tab;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d0 = 32 * db + 8 * e + 4 * hl;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[db * TB + tb][4 * e + i];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const int j = d0 / 2 + pp;
+              float2 cs;
+              if (j < pt) {
+                if (t_in_tab)
+                  cs = tab[tbase + j];
+                else
+                  cs = rope_cos_sin_slow(t0 + f - a.pos_off[b], a.omega_t[j]);
+              } else if (hw_lds) {
+                cs = tab[j < pth ? hbase + j : wbase + j];
+              } else {
+                cs = j < pth ? a.tab_h[yy * dh2 + (j - pt)] : a.tab_w[xx * dw2 + (j - pth)];
+              }
+              const float u = v[2 * pp], w = v[2 * pp + 1];
+              v[2 * pp] = u * cs.x - w * cs.y;
+              v[2 * pp + 1] = u * cs.y + w * cs.x;
+            }
+            uint2 o;
+            o.x = uint32_t(bits16<QT>(v[0])) | (uint32_t(bits16<QT>(v[1])) << 16);
+            o.y = uint32_t(bits16<QT>(v[2])) | (uint32_t(bits16<QT>(v[3])) << 16);
+            const int c = (4 * db + e) ^ (l32 % kChunks);
+            *reinterpret_cast<uint2*>(outst + l32 * (D * 2) + c * 16 + hl * 8) = o;
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // the block is in LDS (this wave only)
+      // read back 16 bytes of one row per lane: rows r = (64 / kChunks) n + lane / kChunks
+#pragma unroll
+      for (int n = 0; n < 32 * kChunks / 64; ++n) {
+        const int r = n * (64 / kChunks) + lane / kChunks, c = lane % kChunks;
+        const uint4 val = *reinterpret_cast<const uint4*>(outst + r * (D * 2) + ((c ^ (r % kChunks)) << 4));
+        const int t = tile0 + r;
+        if (t < Ntok) {
+          const int64_t row = sel == 0 ? int64_t(t) * g.H : ring_row(t);
+          *reinterpret_cast<uint4*>(out_base + row * D + c * 8) = val;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // reads done before the next block overwrites
+    }
+  } else {
+    // lane: feature 32db + l32; tokens 32TB*wq + 32tb + 8e + 4hl + 0..3.
+    // Staging: [D features][32 tokens], 64-byte rows, 16-byte chunk c (8
+    // tokens) of row r at c ^ ((r / 4) % 4); each row then leaves as 8-token
+    // pieces, one 16-byte store where the 8 tokens are 16-byte aligned in one
+    // frame, else token by token.
+    uint16_t* vt = static_cast<uint16_t*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int tile0 = m0 + 32 * TB * wq + 32 * tb;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int d0 = 32 * db + 8 * e + 4 * hl;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[db * TB + tb][4 * e + i];
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const int j = d0 / 2 + pp;
-            float2 cs;
-            if (j < pt)
-              cs = fi < kTabFrames ? tab_t[fi * kMaxAxisPairs + j] : rope_cos_sin(t0 + f - a.pos_off[b], a.omega_t[j]);
-            else if (j < pth)
-              cs = a.tab_h[yy * (g.dh / 2) + (j - pt)];
-            else
-              cs = a.tab_w[xx * (g.dw / 2) + (j - pth)];
-            const float u = v[2 * pp], w = v[2 * pp + 1];
-            v[2 * pp] = u * cs.x - w * cs.y;
-            v[2 * pp + 1] = u * cs.y + w * cs.x;
-          }
-          uint2 o;
-          o.x = uint32_t(bits16<QT>(v[0])) | (uint32_t(bits16<QT>(v[1])) << 16);
-          o.y = uint32_t(bits16<QT>(v[2])) | (uint32_t(bits16<QT>(v[3])) << 16);
-          *reinterpret_cast<uint2*>(dst + d0) = o;
-        }
-    }
-  } else {
-    gemm(std::false_type{});
-    if (!fb_valid) return;
-    // lane: feature 32db + l32; tokens 32TB*wq + 32tb + 8e + 4hl + 0..3
-    uint16_t* vt = static_cast<uint16_t*>(a.cache_v) + (int64_t(b) * g.H + head) * D * g.rows_pad;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      uint16_t* vrow = vt + int64_t(32 * db + l32) * g.rows_pad;
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tk = m0 + 32 * TB * wq + 32 * tb + 8 * e + 4 * hl;
-          if (tk >= Ntok) continue;
           const floatx16_t& c = acc[db * TB + tb];
-          const int f = tk / g.P, p = tk - f * g.P;
-          if ((p & 3) == 0 && p + 3 < g.P && tk + 3 < Ntok) {
-            uint2 o;
-            o.x = uint32_t(bits16<__bf16>(c[4 * e])) | (uint32_t(bits16<__bf16>(c[4 * e + 1])) << 16);
-            o.y = uint32_t(bits16<__bf16>(c[4 * e + 2])) | (uint32_t(bits16<__bf16>(c[4 * e + 3])) << 16);
-            *reinterpret_cast<uint2*>(vrow + slot_of(f) * g.slot_rows + p) = o;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int ti = tk + i;
-              if (ti >= Ntok) break;
-              const int fi2 = ti / g.P, pi = ti - fi2 * g.P;
-              vrow[slot_of(fi2) * g.slot_rows + pi] = bits16<__bf16>(c[4 * e + i]);
-            }
-          }
+          uint2 o;
+          o.x = uint32_t(bits16<__bf16>(c[4 * e])) | (uint32_t(bits16<__bf16>(c[4 * e + 1])) << 16);
+          o.y = uint32_t(bits16<__bf16>(c[4 * e + 2])) | (uint32_t(bits16<__bf16>(c[4 * e + 3])) << 16);
+          const int r = 32 * db + l32;
+          *reinterpret_cast<uint2*>(outst + r * 64 + ((e ^ ((r >> 2) & 3)) << 4) + hl * 8) = o;
         }
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+      for (int n = 0; n < D * 4 / 64; ++n) {
+        const int r = 16 * n + (lane >> 2), c = lane & 3;
+        const uint4 val = *reinterpret_cast<const uint4*>(outst + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+        const int t = tile0 + 8 * c;
+        if (t >= Ntok) continue;
+        uint16_t* vrow = vt + int64_t(r) * g.rows_pad;
+        const int f = t / g.P, p = t - f * g.P;
+        if ((p & 7) == 0 && p + 7 < g.P && t + 7 < Ntok) {
+          *reinterpret_cast<uint4*>(vrow + slot_of(f) * g.slot_rows + p) = val;
+        } else {
+          const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (t + i < Ntok) vrow[ring_row(t + i)] = uint16_t(w4[i / 2] >> (16 * (i & 1)));
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     }
     // stamps: the frames whose first token lies in this tile (one writer:
     // the wave group holding v head 0)
