@@ -14,11 +14,13 @@
 // heads of q, k or v) for 256 or 384 tokens; 8 waves (two per SIMD) of 64
 // or 96 tokens x D features, fp32 accumulators, 32x32x16 bf16 MFMA.  Both
 // operands are K-contiguous in memory (x rows, weight rows) and move global
-// -> LDS with the 16-byte direct loads of gfx950 into a ring of 32-deep K
-// slices (4 stages of 32 KB, or 3 of 40 KB, at D = 128), loaded up to three
-// slices ahead.  Rows of a slice are 64 bytes; the 16-byte chunk c of row r
-// sits at c ^ ((r >> 2) & 3), which puts any 16 consecutive rows of a
-// fragment read on distinct banks.
+// -> LDS with the 16-byte direct loads of gfx950 into two stages of 64-deep
+// K slices (80 KB, or 64 KB, at D = 128): slice kt+1 loads while slice kt is
+// computed, one barrier per slice.  A slice row is 128 bytes, one whole
+// cache line of x or of the weight per load (32-deep slices, half lines,
+// measured 3-7% slower); a d_model that is an odd multiple of 32 ends with
+// a 32-deep slice.  The 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7),
+// which puts any 16 consecutive rows of a fragment read on distinct banks.
 // For q and k the MFMA computes C^T (features as rows) so that each lane
 // holds the dim pairs (2j, 2j+1) of one token, which RoPE rotates in
 // registers; for v it computes C (tokens as rows) so that each lane holds 4
@@ -41,7 +43,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kQK = 32;        // reduction depth of one LDS stage
+constexpr int kQK = 64;        // reduction depth of one LDS slice
 constexpr int kQTokGroups = 4; // waves per feature block
 
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
@@ -61,7 +63,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // byte offset of 16-byte chunk c of row r in a slice (64-byte rows)
-__device__ __forceinline__ int slice_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ int slice_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // fp32 -> T (round to nearest even).  fp16 saturates: a value beyond the
 // largest finite fp16 is stored as +-65504 instead of +-inf, so rotated keys
@@ -83,14 +85,14 @@ __device__ __forceinline__ uint16_t bits16(float x) {
 // features (two heads of q, k or v; the blocks may belong to different
 // ones); 8 waves, two per SIMD, so that one wave's MFMAs cover the other's
 // waits; each wave computes 32*TB tokens of one block.  TB = 3 (384 tokens,
-// a 3-stage ring) gives fewer, larger workgroups than TB = 2 (256 tokens, a
-// 4-stage ring); the host picks the one whose grid fills the chip better.
+// 160 KB of LDS) gives fewer, larger workgroups than TB = 2 (256 tokens);
+// the host picks the one whose grid fills the chip better.
 // (4 waves of 128x128 tiles -- half the LDS bytes per MFMA -- measured 1.5x
 // slower: a lone wave per SIMD stalls on its own loads.)
 template <typename QT, int D, int TB>
 __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   constexpr int kQM = 32 * TB * kQTokGroups;   // tokens per workgroup
-  constexpr int kQStages = TB >= 3 ? 3 : 4;
+  constexpr int kQStages = 2;
   constexpr int kTokGroups = kQTokGroups;
   constexpr int kQWaves = 2 * kTokGroups;
   constexpr int kThreads = 64 * kQWaves;
@@ -140,55 +142,67 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const char* xbase = static_cast<const char*>(a.x) + int64_t(b) * Ntok * Dm * 2;
   const char* wbase = static_cast<const char*>(a.w) + int64_t(fb0) * D * Dm * 2;
   const int w_rows = min(2, n_blocks - fb0) * D;  // weight rows that exist
-  uint32_t xo[X_DMA], wo[W_DMA];
+  // hi: bit j set where load j of this lane fetches a chunk of the second
+  // half of the 128-byte row piece (moved back by 64 bytes in a final
+  // 32-deep slice, whose second half lies past the end of the row)
+  uint32_t xo[X_DMA], wo[W_DMA], hi = 0;
 #pragma unroll
   for (int j = 0; j < X_DMA; ++j) {
-    const int piece = (wave * X_DMA + j) * 64 + lane, r = piece >> 2, cs = piece & 3;
+    const int piece = (wave * X_DMA + j) * 64 + lane, r = piece >> 3, c = (piece & 7) ^ ((r >> 1) & 7);
     const int tok = min(m0 + r, Ntok - 1);  // rows past the last token repeat it (outputs dropped)
-    xo[j] = uint32_t(tok) * uint32_t(Dm * 2) + uint32_t((cs ^ ((r >> 2) & 3)) << 4);
+    xo[j] = uint32_t(tok) * uint32_t(Dm * 2) + uint32_t(c << 4);
+    hi |= uint32_t(c >> 2) << j;
   }
 #pragma unroll
   for (int j = 0; j < W_DMA; ++j) {
-    const int piece = (wave * W_DMA + j) * 64 + lane, r = piece >> 2, cs = piece & 3;
+    const int piece = (wave * W_DMA + j) * 64 + lane, r = piece >> 3, c = (piece & 7) ^ ((r >> 1) & 7);
     const int rr = min(r, w_rows - 1);  // a missing second block repeats the last row (unused)
-    wo[j] = uint32_t(rr) * uint32_t(Dm * 2) + uint32_t((cs ^ ((r >> 2) & 3)) << 4);
+    wo[j] = uint32_t(rr) * uint32_t(Dm * 2) + uint32_t(c << 4);
+    hi |= uint32_t(c >> 2) << (X_DMA + j);
   }
+  const int n_full = Dm / kQK;              // 64-deep slices
+  const bool half_tail = Dm % kQK != 0;     // then one more, 32 deep
+  // LDS: the x stages [2][XB], then the weight stages [2][WB], so that every
+  // fragment read reaches its stage with an immediate offset below 64 KB
   auto issue = [&](int kt, int stg) {
-    const uint32_t dst = lds0 + uint32_t(stg * STAGE);
     const int64_t k0 = int64_t(kt) * kQK * 2;
+    const uint32_t back = kt == n_full ? hi : 0u;  // the 32-deep slice: second-half chunks repeat the first half
 #pragma unroll
-    for (int j = 0; j < X_DMA; ++j) dma16(uniform_ptr(xbase + k0), xo[j], dst + uint32_t((wave * X_DMA + j) * 1024));
+    for (int j = 0; j < X_DMA; ++j)
+      dma16(uniform_ptr(xbase + k0), xo[j] - (((back >> j) & 1u) << 6),
+            lds0 + uint32_t(stg * XB + (wave * X_DMA + j) * 1024));
 #pragma unroll
-    for (int j = 0; j < W_DMA; ++j) dma16(uniform_ptr(wbase + k0), wo[j], dst + uint32_t(XB + (wave * W_DMA + j) * 1024));
+    for (int j = 0; j < W_DMA; ++j)
+      dma16(uniform_ptr(wbase + k0), wo[j] - (((back >> (X_DMA + j)) & 1u) << 6),
+            lds0 + uint32_t(2 * XB + stg * WB + (wave * W_DMA + j) * 1024));
   };
 
   floatx16_t acc[DB * TB];
 #pragma unroll
   for (int i = 0; i < DB * TB; ++i) acc[i] = floatx16_t{};
 
-  // fragment offsets inside a stage (chunk 2*kk + hl of the row)
-  int xoff[2][TB], woff[2][DB];
+  // this lane's fragment offsets in stage 0 (chunk 2*kk + hl of the row); a
+  // 32-row block adds 4096 bytes, a stage XB or WB
+  int xoff[4], woff[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xoff[kk][tb] = slice_off(32 * TB * wq + 32 * tb + l32, 2 * kk + hl);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) woff[kk][db] = XB + slice_off(D * grp + 32 * db + l32, 2 * kk + hl);
+  for (int kk = 0; kk < 4; ++kk) {
+    xoff[kk] = slice_off(32 * TB * wq + l32, 2 * kk + hl);
+    woff[kk] = 2 * XB + slice_off(D * grp + l32, 2 * kk + hl);
   }
 
   // Every wave passes the same barriers; the MFMA operand order (C^T for q
-  // and k, C for v) is per wave.  Fragments of the next 16-deep step are read
-  // while the MFMAs of the current one run, also across the barrier that
-  // publishes the next slice: a trip reads step 1 of slice kt, runs step 0,
-  // waits for slice kt+1, reads its step 0 and runs step 1 of slice kt.
+  // and k, C for v) is per wave.  A wave reads the fragments of a 16-deep
+  // step and then runs its MFMAs; the SIMD's other wave covers the wait.
   struct Frags {
     bf16x8_t x[TB], w[DB];
   };
-  auto read = [&](const char* st, int kk, Frags& f) {
+  auto read = [&](int stg, int kk, Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) f.x[tb] = *reinterpret_cast<const bf16x8_t*>(st + xoff[kk][tb]);
+    for (int tb = 0; tb < TB; ++tb)
+      f.x[tb] = *reinterpret_cast<const bf16x8_t*>(smem + xoff[kk] + stg * XB + tb * 4096);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) f.w[db] = *reinterpret_cast<const bf16x8_t*>(st + woff[kk][db]);
+    for (int db = 0; db < DB; ++db)
+      f.w[db] = *reinterpret_cast<const bf16x8_t*>(smem + woff[kk] + stg * WB + db * 4096);
   };
   auto gemm = [&](auto trans_tag) {
     constexpr bool kTrans = decltype(trans_tag)::value;  // C^T: features as rows
@@ -203,54 +217,42 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
             acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[tb], f.w[db], acc[db * TB + tb], 0, 0, 0);
         }
     };
-    const int n_k = Dm / kQK;
-    // wait until slice kt has landed (slices after it may still be loading)
-    auto wait_slice = [&](int kt) {
-      const int ahead = min(n_k - 1 - kt, kQStages - 2);
-      if (ahead >= 2)
-        wait_vm<2 * DMA>();
-      else if (ahead == 1)
+    const int n_k = n_full + (half_tail ? 1 : 0);
+    // two stages: slice kt+1 loads while slice kt is computed
+    issue(0, 0);
+    if (n_k > 1) issue(1, 1);
+    // slice kt in stage kt % 2 (a constant: the loop is unrolled twice)
+    auto slice = [&](auto stg_c, int kt) __attribute__((always_inline)) {
+      constexpr int stg = decltype(stg_c)::value;
+      // the offsets pass through an empty asm each slice, so that offset +
+      // stage is formed at the read (as its immediate) instead of being
+      // hoisted out of the loop into registers
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        asm volatile("" : "+v"(xoff[kk]));
+        asm volatile("" : "+v"(woff[kk]));
+      }
+      if (kt == 0 && n_k > 1)
         wait_vm<DMA>();
       else
         wait_vm<0>();
+      __syncthreads();  // slice kt landed everywhere; slice kt-1 is done everywhere
+      if (kt >= 1 && kt + 1 < n_k) issue(kt + 1, stg ^ 1);
+      const int n_kk = kt == n_full ? 2 : 4;  // 16-deep steps in this slice
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk >= n_kk) break;
+        Frags f;
+        read(stg, kk, f);
+        mma(f);
+      }
     };
-#pragma unroll
-    for (int i = 0; i < kQStages - 1; ++i)
-      if (i < n_k) issue(i, i);
-    if constexpr (TB >= 3) {
-      // 96-token waves: no registers for a second fragment set; the SIMD's
-      // other wave covers the fragment waits
-      for (int kt = 0; kt < n_k; ++kt) {
-        wait_slice(kt);
-        __syncthreads();  // slice kt landed everywhere; slice kt-1 is done everywhere
-        if (kt + kQStages - 1 < n_k) issue(kt + kQStages - 1, (kt + kQStages - 1) % kQStages);
-        const char* st = smem + (kt % kQStages) * STAGE;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          Frags f;
-          read(st, kk, f);
-          mma(f);
-        }
-      }
-      return;
+    int kt = 0;
+    for (; kt + 2 <= n_k; kt += 2) {
+      slice(std::integral_constant<int, 0>{}, kt);
+      slice(std::integral_constant<int, 1>{}, kt + 1);
     }
-    wait_slice(0);
-    __syncthreads();
-    if (kQStages - 1 < n_k) issue(kQStages - 1, kQStages - 1);
-    Frags f0, f1;
-    read(smem, 0, f0);
-    for (int kt = 0; kt < n_k; ++kt) {
-      const char* st = smem + (kt % kQStages) * STAGE;
-      read(st, 1, f1);
-      mma(f0);
-      if (kt + 1 < n_k) {
-        wait_slice(kt + 1);
-        __syncthreads();  // slice kt+1 landed everywhere; slice kt-1... kt's reads are done everywhere
-        if (kt + kQStages < n_k) issue(kt + kQStages, (kt + kQStages) % kQStages);
-        read(smem + ((kt + 1) % kQStages) * STAGE, 0, f0);
-      }
-      mma(f1);
-    }
+    if (kt < n_k) slice(std::integral_constant<int, 0>{}, kt);
   };
 
   const int64_t t0 = a.t0[b];
