@@ -363,8 +363,10 @@ def time_qkv(r, w, reps=20):
 
 def time_refresh_and_sink(r, w, reps=20):
     """HIP-event times of the RoPE refresh (every cached key's time pairs,
-    one launch) and of a one-frame sink update, on the launch stream, after
-    the timed steps (they change the cache state the steps ran on)."""
+    one launch), of a one-frame sink update (its own launch), and of the
+    chunk's append with and without its last frame also written into the
+    sink (one launch), on the launch stream, after the timed steps (they
+    change the cache state the steps ran on)."""
     import torch
 
     eb = 2 if w.dtype == "bf16" else 4
@@ -375,10 +377,18 @@ def time_refresh_and_sink(r, w, reps=20):
     k1 = r.k[:, :P].contiguous()
     v1 = r.v[:, :P].contiguous()
     first = list(w.t0)
+    nq = w.query_frames
+    append_bytes = 6 * B * w.query_rows * H * D * eb
+    fused_bytes = append_bytes + 2 * B * P * H * D * eb  # + the sink frame's k_rot and v^T writes
     res = {}
     for name, fn, nbytes in (
         # the sink update first: the refreshes move time positions below t0
         ("sink_update", lambda: r.cache.sink_update(k1, v1, first, 1), sink_bytes),
+        # the chunk's append with its last frame also written into sink slot 0
+        # (one launch): compare with "append" for the sink update's marginal cost
+        ("append", lambda: r.cache.rope3d_append(r.q, r.q_rot, r.k, r.v, first, nq), append_bytes),
+        ("append_with_sink", lambda: r.cache.rope3d_append_sink(r.q, r.q_rot, r.k, r.v, first, nq, nq - 1, 1),
+         fused_bytes),
         ("rope_refresh", lambda: r.cache.rope_refresh([1] * B), refresh_bytes),
     ):
         fn()
@@ -392,6 +402,7 @@ def time_refresh_and_sink(r, w, reps=20):
         us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / reps
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us": us, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    res["append_with_sink"]["sink_marginal_us"] = res["append_with_sink"]["us"] - res["append"]["us"]
     return res
 
 

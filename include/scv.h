@@ -226,6 +226,23 @@ scv_status scv_time_offsets(const scv_cache* c, int64_t* out);
 scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int64_t* first_frame, int32_t n_frames,
                            void* stream);
 
+/* scv_rope3d_append and a sink update from the same chunk in one launch (the
+ * sink refreshed from recent content, as for scv_sink_update; the fusion of
+ * neighbouring operators as in the Causal-RoPE SP paper, section 2(c)).  The
+ * result equals scv_rope3d_append(c, q, q_rot, k, v, t0, n_frames) followed
+ * by scv_sink_update on frames sink_first .. sink_first+sink_frames-1 of the
+ * same k and v (first_frame[b] = t0[b] + sink_first): those frames' rotated
+ * keys and values are written a second time, into sink slots 0 ..
+ * sink_frames-1, which are stamped with the frames; nothing is read twice.
+ * Needs sink_frames in [1, cache sink_frames], sink_first >= 0,
+ * sink_first + sink_frames <= n_frames and every t0[b] >= the cache's
+ * sink_frames (a chunk whose own frames would land in sink slots is
+ * refused with SCV_E_RANGE: its two writes would target the same slot).
+ * Other rules and errors as for scv_rope3d_append. */
+scv_status scv_rope3d_append_sink(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
+                                  const int64_t* t0, int32_t n_frames, int32_t sink_first, int32_t sink_frames,
+                                  void* stream);
+
 /* Schedule chunk_attention will use for this request: a key split count
  * >= 1 (grid schedule: one workgroup per query tile, head and split), or
  * SCV_SCHEDULE_BALANCED = -1 (bf16 only: the work, counted in query-tile x

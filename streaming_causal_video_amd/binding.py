@@ -87,6 +87,10 @@ _SIGNATURES = {
     "scv_rope_refresh": (ctypes.c_int, [_VP, _I64P, _VP]),
     "scv_time_offsets": (ctypes.c_int, [_VP, _I64P]),
     "scv_sink_update": (ctypes.c_int, [_VP, _VP, _VP, _I64P, ctypes.c_int32, _VP]),
+    "scv_rope3d_append_sink": (
+        ctypes.c_int,
+        [_VP, _VP, _VP, _VP, _VP, _I64P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP],
+    ),
     "scv_attention_splits": (ctypes.c_int32, [_VP, _I64P, ctypes.c_int32, ctypes.c_int32, ctypes.c_size_t]),
     "scv_attention_workspace_bytes": (ctypes.c_size_t, [_VP, ctypes.c_int32, ctypes.c_int32]),
     "scv_attention_request_workspace_bytes": (ctypes.c_size_t, [_VP, _I64P, ctypes.c_int32, ctypes.c_int32]),
@@ -311,6 +315,20 @@ class Cache:
             self.lib.scv_sink_update(self.handle, _ptr(k), _ptr(v), _t0_array(first_frame, self.cfg.batch), n_frames,
                                      _stream(stream)),
             "scv_sink_update",
+        )
+
+    def rope3d_append_sink(self, q, q_rot, k, v, t0, n_frames, sink_first, sink_frames, stream=None):
+        """rope3d_append, and frames sink_first .. sink_first+sink_frames-1 of
+        the same k, v also written into sink slots 0 .. sink_frames-1."""
+        self._tok(q, n_frames, "q")
+        self._tok(q_rot, n_frames, "q_rot", rotated=True)
+        self._tok(k, n_frames, "k")
+        self._tok(v, n_frames, "v")
+        _check(
+            self.lib.scv_rope3d_append_sink(self.handle, _ptr(q), _ptr(q_rot), _ptr(k), _ptr(v),
+                                            _t0_array(t0, self.cfg.batch), n_frames, int(sink_first),
+                                            int(sink_frames), _stream(stream)),
+            "scv_rope3d_append_sink",
         )
 
     SCHEDULE_BALANCED = -1

@@ -158,6 +158,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 
   int64_t slot = 0;
   if (to_cache) slot = a.to_sink ? f : (gframe < g.S_f ? gframe : g.S_f + gframe % g.R);
+  // append + sink update in one launch: this frame is also written to sink
+  // slot sslot (same rotated k, same v)
+  const int sslot = f - a.sink_first;
+  const bool also_sink = to_cache && !a.to_sink && sslot >= 0 && sslot < a.sink_frames;
 
   __syncthreads();
 
@@ -214,6 +218,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
         const int64_t row = slot * g.slot_rows + p;
         QT* dst = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + row) * D + dg * EPV;
         *reinterpret_cast<uint4*>(dst) = outv;
+        if (also_sink) *reinterpret_cast<uint4*>(dst + (int64_t(sslot) - slot) * g.slot_rows * D) = outv;
       } else {
         *reinterpret_cast<uint4*>(static_cast<QT*>(a.k_out) + in_off) = outv;
       }
@@ -253,10 +258,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
         out = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
       }
       *reinterpret_cast<uint4*>(vbase + int64_t(d) * g.rows_pad + c * EPV) = out;
+      if (also_sink) *reinterpret_cast<uint4*>(vbase + int64_t(d) * g.rows_pad + c * EPV + (int64_t(sslot) - slot) * g.slot_rows) = out;
     }
   }
 
-  if (to_cache && tile == 0 && head == 0 && threadIdx.x == 0) a.stamps[int64_t(b) * g.n_slots + slot] = gframe;
+  if (to_cache && tile == 0 && head == 0 && threadIdx.x == 0) {
+    a.stamps[int64_t(b) * g.n_slots + slot] = gframe;
+    if (also_sink) a.stamps[int64_t(b) * g.n_slots + sslot] = gframe;
+  }
 }
 
 // RoPE refresh: every cached key row of stream b, head h (all rows_pad rows:

@@ -651,6 +651,44 @@ scv_status scv_sink_update(scv_cache* c, const void* k, const void* v, const int
   }
 }
 
+scv_status scv_rope3d_append_sink(scv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
+                                  const int64_t* t0, int32_t n_frames, int32_t sink_first, int32_t sink_frames,
+                                  void* stream) {
+  try {
+    scv_status s;
+    if ((s = check_cache(c)) != SCV_OK) return s;
+    if ((q == nullptr) != (q_rot == nullptr)) return fail(SCV_E_INVALID, "give both q and q_rot or neither");
+    if ((s = check_ptr(q, "q", false)) != SCV_OK) return s;
+    if ((s = check_ptr(q_rot, "q_rot", false)) != SCV_OK) return s;
+    if ((s = check_ptr(k, "k", true)) != SCV_OK) return s;
+    if ((s = check_ptr(v, "v", true)) != SCV_OK) return s;
+    if ((s = check_times(c, t0, n_frames < 1 ? 1 : n_frames)) != SCV_OK) return s;
+    if ((s = check_append_frames(c, t0, n_frames)) != SCV_OK) return s;
+    if ((s = check_positions(c, t0, n_frames)) != SCV_OK) return s;
+    if (c->g.S_f < 1) return fail(SCV_E_SHAPE, "the cache has no sink slots (sink_frames == 0)");
+    if (sink_frames < 1 || sink_frames > c->g.S_f)
+      return fail(SCV_E_SHAPE, "sink_frames must be in [1, " + std::to_string(c->g.S_f) + "]");
+    if (sink_first < 0 || int64_t(sink_first) + sink_frames > n_frames)
+      return fail(SCV_E_SHAPE, "sink_first + sink_frames must lie inside the call's n_frames frames");
+    for (int b = 0; b < c->g.B; ++b)
+      if (t0[b] < c->g.S_f)
+        return fail(SCV_E_RANGE, "t0[" + std::to_string(b) + "] = " + std::to_string(t0[b]) +
+                                     " would append into a sink slot; the fused sink update needs t0 >= sink_frames");
+    scv::RopeArgs a = base_rope_args(c, t0, n_frames);
+    set_cache_targets(c, &a);
+    a.q_in = q;
+    a.q_out = q_rot;
+    a.k_in = k;
+    a.v_in = v;
+    a.rotate_k = 1;
+    a.sink_first = sink_first;
+    a.sink_frames = sink_frames;
+    return hip_status(scv::launch_rope_append(a, static_cast<hipStream_t>(stream)), "rope3d_append_sink launch");
+  } catch (...) {
+    return fail(SCV_E_INVALID, "internal error");
+  }
+}
+
 scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, const void* w_qkv, void* q_rot,
                                const int64_t* t0, int32_t n_frames, void* stream) {
   try {

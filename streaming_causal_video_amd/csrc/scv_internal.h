@@ -53,6 +53,8 @@ struct RopeArgs {
   int32_t n_frames;
   int32_t rotate_k;  // 0: k is already rotated (kv_append_roll)
   int32_t to_sink;   // 1: frame f of the call goes to sink slot f (sink update)
+  int32_t sink_first;   // with sink_frames > 0: frames sink_first .. +sink_frames-1 of the
+  int32_t sink_frames;  // call also go to sink slots 0 .. sink_frames-1 (append + sink update)
   Geometry g;
   int64_t t0[kMaxBatch];       // global frame of the call's first frame
   int64_t pos_off[kMaxBatch];  // time position = global frame - pos_off

@@ -306,6 +306,27 @@ def test_balanced_schedule_plan(lib):
     lib.scv_cache_destroy(h)
 
 
+def test_append_sink_validation(lib):
+    cfg, h = make_handle(lib, sink_frames=2)
+    p = FAKE + (1 << 36)
+
+    def call(t, n, first, count, q_rot=p):
+        return lib.scv_rope3d_append_sink(h, p, q_rot, p, p, t, n, first, count, None)
+
+    assert call(t0(5), 3, 0, 1, q_rot=None) == -1     # q without q_rot
+    assert call(t0(5), 3, 0, 0) == -2                 # no sink frame
+    assert call(t0(5), 3, 0, 3) == -2                 # more than the cache's sink slots
+    assert call(t0(5), 3, -1, 1) == -2                # before the call's first frame
+    assert call(t0(5), 3, 2, 2) == -2                 # past the call's last frame
+    assert call(t0(1), 3, 0, 1) == -5                 # the chunk itself would land in a sink slot
+    assert call(t0(-5), 3, 0, 1) == -5
+    assert B.last_error()
+    lib.scv_cache_destroy(h)
+    cfg, h = make_handle(lib, sink_frames=0)
+    assert lib.scv_rope3d_append_sink(h, p, p, p, p, t0(5), 3, 0, 1, None) == -2  # no sink slots at all
+    lib.scv_cache_destroy(h)
+
+
 def test_qkv_validation(lib):
     cfg, h = make_handle(lib)
     p = FAKE + (1 << 36)

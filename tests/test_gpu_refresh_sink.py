@@ -236,6 +236,65 @@ def test_sink_update_480p(gpu_lib):
     sink_update_case(w, w.chunk_frames - 1, 1, rows=sample_rows(w.query_rows, 33, n_random=96))
 
 
+def append_sink_case(w, sink_first, n_sink, rows=None):
+    """rope3d_append with a sink update from the same chunk in one launch:
+    bit-exact against the two separate calls, and against the oracle's
+    rope3d_append followed by its sink_update."""
+    import torch
+
+    P = w.tokens_per_frame
+    fused = StreamRunner(w)
+    fused.fill()
+    fused.cache.rope3d_append_sink(fused.q, fused.q_rot, fused.k, fused.v, list(w.t0), w.query_frames, sink_first,
+                                   n_sink)
+    sep = StreamRunner(w)
+    sep.fill()
+    sep.append()
+    sel = slice(sink_first * P, (sink_first + n_sink) * P)
+    first = [t + sink_first for t in w.t0]
+    sep.cache.sink_update(sep.k[:, sel].contiguous(), sep.v[:, sel].contiguous(), first, n_sink)
+    torch.cuda.synchronize()
+    vf, vs = fused.cache.views(), sep.cache.views()
+    for key in ("k", "v_t", "stamps"):
+        assert torch.equal(vf[key], vs[key]), key
+    assert torch.equal(fused.q_rot, sep.q_rot)
+    oc, q_ref = oracle_replay(w)
+    oc.sink_update(G.frames_tensor(w, G.TENSOR_K, first, n_sink), G.frames_tensor(w, G.TENSOR_V, first, n_sink),
+                   first, n_sink)
+    assert np.array_equal(vf["stamps"].cpu().numpy(), oc.stamps)
+    L = fused.cache.layout
+    for b in range(w.batch):
+        for s in range(n_sink):
+            rws = slice(s * L.slot_rows, s * L.slot_rows + P)
+            check_rounding(f"sink {s} k", to_np(vf["k"][b, :, rws, :]).transpose(1, 0, 2), oc.k[b][s], qk(w))
+            assert np.array_equal(to_np(vf["v_t"][b, :, :, rws]).transpose(2, 0, 1), oc.v[b][s])
+    fused.attend()
+    torch.cuda.synchronize()
+    attention_check(fused, oc, q_ref, w, rows=rows)
+
+
+APPEND_SINK_CASES = [
+    (small("append-sink-b2", batch=2, heads=3, grid_h=6, grid_w=10, chunk_frames=3, window_frames=5, t0=(230, 40),
+           sink_frames=2, seed=221), 1, 2),
+    (small("append-sink-fp32", dtype="fp32", head_dim=64, split=(24, 20, 20), grid_h=5, grid_w=7, t0=(77,),
+           seed=222), 1, 1),
+    (small("append-sink-qkfp16", grid_h=6, grid_w=8, t0=(3000,), qk_dtype="fp16", seed=223), 0, 1),
+    (small("append-sink-odd-grid", grid_h=3, grid_w=5, chunk_frames=3, t0=(12,), seed=224), 2, 1),
+]
+
+
+@pytest.mark.parametrize("w,first,n", APPEND_SINK_CASES, ids=[c[0].name for c in APPEND_SINK_CASES])
+def test_append_sink_parity(w, first, n, gpu_lib):
+    say(f"case append+sink {w.name} first={first} n={n}")
+    append_sink_case(w, first, n)
+
+
+def test_append_sink_480p(gpu_lib):
+    w = W.WAN13B_480P
+    say(f"case append+sink {w.name}")
+    append_sink_case(w, w.chunk_frames - 1, 1, rows=sample_rows(w.query_rows, 34, n_random=96))
+
+
 @pytest.mark.parametrize("dtype,kv_splits", [("bf16", 0), ("fp32", 0), ("bf16", -1)])
 def test_stream_with_refresh_and_sink_updates(dtype, kv_splits, gpu_lib):
     """A stream of 24 chunks from t0 = 0 with a RoPE refresh every 5 chunks
