@@ -333,12 +333,28 @@ def ablations(w):
     print(json.dumps(out), flush=True)
 
 
+def back_to_back_us(fn, reps):
+    """Mean time per launch of reps back-to-back launches of fn, from one
+    pair of HIP events on the launch stream around all of them (a pair
+    around each launch would add the launch latency of an idle queue to
+    every one: ~10 us on a 80 us projection)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / reps
+
+
 def time_qkv(r, w, reps=20):
     """HIP-event time of the QKV projection fused with RoPE and the append
     (d_model = heads * head_dim, the Wan layers' width), replacing the
     step's rope3d_append: FLOPs 2 * tokens * d_model * 3*H*d."""
-    import torch
-
     from streaming_causal_video_amd import datagen as G
     from streaming_causal_video_amd.runner import to_device
 
@@ -347,15 +363,7 @@ def time_qkv(r, w, reps=20):
     x = to_device(G.hidden_frames(w, d_model, w.t0, n), "bf16")
     wq = to_device(G.qkv_weight(w, d_model), "bf16")
     fn = lambda: r.cache.qkv_rope_append(x, wq, r.q_rot, w.t0, n)  # noqa: E731
-    fn()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record()
-        fn()
-        b.record()
-    torch.cuda.synchronize()
-    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / reps
+    us = back_to_back_us(fn, reps)
     flops = 2.0 * w.batch * w.query_rows * d_model * 3 * w.heads * w.head_dim
     tf = flops / (us * 1e-6) / 1e12
     return {"us": us, "d_model": d_model, "flops": flops, "tflops": tf, "frac_mfma": tf / PEAK_TFLOPS["bf16"]}
@@ -367,8 +375,6 @@ def time_refresh_and_sink(r, w, reps=20):
     chunk's append with and without its last frame also written into the
     sink (one launch), on the launch stream, after the timed steps (they
     change the cache state the steps ran on)."""
-    import torch
-
     eb = 2 if w.dtype == "bf16" else 4
     P, H, D, B = w.tokens_per_frame, w.heads, w.head_dim, w.batch
     cached_rows = w.n_slots * P  # every slot holds a frame in the steady state
@@ -381,7 +387,7 @@ def time_refresh_and_sink(r, w, reps=20):
     append_bytes = 6 * B * w.query_rows * H * D * eb
     fused_bytes = append_bytes + 2 * B * P * H * D * eb  # + the sink frame's k_rot and v^T writes
     res = {}
-    for name, fn, nbytes in (
+    cases = [
         # the sink update first: the refreshes move time positions below t0
         ("sink_update", lambda: r.cache.sink_update(k1, v1, first, 1), sink_bytes),
         # the chunk's append with its last frame also written into sink slot 0
@@ -390,19 +396,15 @@ def time_refresh_and_sink(r, w, reps=20):
         ("append_with_sink", lambda: r.cache.rope3d_append_sink(r.q, r.q_rot, r.k, r.v, first, nq, nq - 1, 1),
          fused_bytes),
         ("rope_refresh", lambda: r.cache.rope_refresh([1] * B), refresh_bytes),
-    ):
-        fn()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in ev:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / reps
+    ]
+    if min(w.t0) < w.sink_frames:  # a chunk that lands in sink slots cannot also refresh them
+        cases = [c for c in cases if c[0] != "append_with_sink"]
+    for name, fn, nbytes in cases:
+        us = back_to_back_us(fn, reps)
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us": us, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
-    res["append_with_sink"]["sink_marginal_us"] = res["append_with_sink"]["us"] - res["append"]["us"]
+    if "append_with_sink" in res:
+        res["append_with_sink"]["sink_marginal_us"] = res["append_with_sink"]["us"] - res["append"]["us"]
     return res
 
 
