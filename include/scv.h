@@ -251,6 +251,15 @@ scv_status scv_rope3d_append_sink(scv_cache* c, const void* q, void* q_rot, cons
  * query tile's key walk; a query tile cut by range boundaries leaves fp32
  * partials that a merge kernel combines -- this keeps every compute unit
  * busy when the query tiles do not fill whole rounds of the chip).
+ * SCV_SCHEDULE_ROUNDS = -2 is the balanced schedule with whole-item rounds
+ * (bf16 only, all query tiles visiting the same number of key tiles, more
+ * of them than compute units): the first rounds run whole query tiles, one
+ * per workgroup, with the compute units of an XCD on consecutive query
+ * tiles of a head so that they share its keys and values in L2, and only
+ * the query tiles left over are cut into equal ranges -- far less HBM
+ * traffic (the 720p layer: 3.1x instead of 10.7x the algorithmic bytes) for
+ * 1-2% more time, so kv_splits = 0 never picks it; where it does not apply
+ * it falls back to -1.
  * kv_splits > 0 asks for that many splits (capped at 64 and at the number
  * of 64-key tiles); kv_splits = -1 asks for the balanced schedule (the fp32
  * path, and tiles too short for it, fall back to one split).  kv_splits = 0
@@ -261,11 +270,12 @@ scv_status scv_rope3d_append_sink(scv_cache* c, const void* q, void* q_rot, cons
  * ws_bytes are considered (SIZE_MAX: no limit).  Returns 0 on invalid
  * arguments. */
 #define SCV_SCHEDULE_BALANCED (-1)
+#define SCV_SCHEDULE_ROUNDS (-2)
 int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
                              size_t ws_bytes);
 
 /* Workspace bytes chunk_attention needs for this request with
- * kv_splits > 0 or -1 (steady-state key counts), or the most the
+ * kv_splits > 0, -1 or -2 (steady-state key counts), or the most the
  * steady-state choice of kv_splits = 0 needs (0 when it runs without
  * splits).  With kv_splits = 0, chunk_attention picks among the schedules
  * this workspace (and t0) allows. */
@@ -290,7 +300,7 @@ size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* 
  * rounded to the dtype before PV.  With more than one split, or the
  * balanced schedule, the pieces of a query tile write normalised fp32
  * partials into ws (256-byte aligned) and a merge kernel combines them
- * (lse-weighted).  kv_splits (-1, 0 or a split count) chooses as
+ * (lse-weighted).  kv_splits (-2, -1, 0 or a split count) chooses as
  * scv_attention_splits(c, t0, n_frames, kv_splits, ws ? ws_bytes : 0)
  * does; a forced schedule whose workspace exceeds ws_bytes fails with
  * SCV_E_WORKSPACE. */
@@ -304,7 +314,7 @@ scv_status scv_chunk_attention(const scv_cache* c, const void* q_rot, const int6
  * the library holds on every GPU it runs on until the process ends.  The
  * call allocates nothing (no hipMalloc, no allocating library routine).
  * kv_splits = 0 chooses among the schedules whose workspace fits the
- * scratch; a forced schedule (kv_splits > 0 or -1) that needs more fails
+ * scratch; a forced schedule (kv_splits > 0, -1 or -2) that needs more fails
  * with SCV_E_WORKSPACE and nothing enqueued.  Every call on a GPU shares
  * that GPU's scratch: calls whose executions overlap on one GPU (several
  * streams, several threads) race and must be serialised by the caller.

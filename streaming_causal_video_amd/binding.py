@@ -332,6 +332,7 @@ class Cache:
         )
 
     SCHEDULE_BALANCED = -1
+    SCHEDULE_ROUNDS = -2
 
     def attention_splits(self, n_frames, kv_splits=0, t0=None, ws_bytes=None) -> int:
         """Schedule chunk_attention uses: a split count, or -1 for the

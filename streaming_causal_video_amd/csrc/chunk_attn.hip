@@ -449,19 +449,45 @@ __device__ __forceinline__ LeanItem lean_item_by_index(const AttnArgs& a, int id
   return it;
 }
 
-// First unit of workgroup range v, and the range holding unit u.
+// Index of the item holding unit u (items numbered as lean_item_by_index).
+template <int ROWS>
+__device__ __forceinline__ int lean_item_index_at(const AttnArgs& a, int64_t u) {
+  const LeanItem it = lean_item_at<ROWS>(a, u);
+  const int nch = a.n_qtiles / a.qtiles_per_chunk;
+  int per_head_items = 0, before = 0;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int n = chunk_qtiles<ROWS>(a, ch);
+    if (ch < it.chunk) before += n;
+    per_head_items += n;
+  }
+  return (it.b * a.g.H + it.head) * per_head_items + before + it.tile;
+}
+
+// First unit of workgroup range v, and the range holding unit u: ranges
+// below lean_v0 are whole items, the rest cut the remaining units equally.
 __device__ __forceinline__ int64_t lean_range_start(const AttnArgs& a, int v) {
-  return int64_t(v) * a.lean_units / a.lean_ctas;
+  if (v < a.lean_v0) return lean_item_by_index<kRowsBf16>(a, v).start;
+  return a.lean_u0 + int64_t(v - a.lean_v0) * (a.lean_units - a.lean_u0) / (a.lean_ctas - a.lean_v0);
 }
 __device__ __forceinline__ int lean_range_of(const AttnArgs& a, int64_t u) {
-  return int(((u + 1) * a.lean_ctas - 1) / a.lean_units);
+  if (u < a.lean_u0) return lean_item_index_at<kRowsBf16>(a, u);
+  const int nt = a.lean_ctas - a.lean_v0;
+  return a.lean_v0 + int(((u - a.lean_u0 + 1) * nt - 1) / (a.lean_units - a.lean_u0));
 }
-// Workgroup blockIdx.x runs range v: the ranges of one XCD (workgroups are
-// dealt to the 8 XCDs round robin) are consecutive, so the items of a head
-// mostly stay in one L2.
-__device__ __forceinline__ int lean_range_index() {
-  const int c = blockIdx.x, G = gridDim.x;
-  return (G % kXcds == 0) ? (c % kXcds) * (G / kXcds) + c / kXcds : c;
+// Workgroup blockIdx.x runs range v.  Workgroups go to the 8 XCDs round
+// robin; the cut ranges of one XCD are consecutive, so the items of a head
+// mostly stay in one L2; whole-item ranges are renumbered the same way
+// inside each round of lean_round workgroups, so that an XCD's compute
+// units run consecutive query tiles of a head side by side, walking the
+// same key tiles at the same time.
+__device__ __forceinline__ int lean_range_index(const AttnArgs& a) {
+  const int c = blockIdx.x;
+  if (c < a.lean_v0) {
+    const int R = a.lean_round, r = c / R, k = c - r * R;
+    return (R % kXcds == 0) ? r * R + (k % kXcds) * (R / kXcds) + k / kXcds : c;
+  }
+  const int G = a.lean_ctas - a.lean_v0, t = c - a.lean_v0;
+  return a.lean_v0 + ((G % kXcds == 0) ? (t % kXcds) * (G / kXcds) + t / kXcds : t);
 }
 
 template <int D, typename QKT>
@@ -1023,7 +1049,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     sg.partial = a.splits > 1;
     sg.prow = ((int64_t(split) * g.B + sg.b) * g.H + sg.head) * a.Nq;
   } else {
-    lean_v = lean_range_index();
+    lean_v = lean_range_index(a);
     lean_lo = lean_range_start(a, lean_v);
     lean_hi = lean_range_start(a, lean_v + 1);
     if (lean_hi <= lean_lo) return;

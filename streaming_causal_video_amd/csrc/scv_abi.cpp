@@ -294,30 +294,63 @@ void class_units(const scv_cache* c, const int64_t* t0, int32_t n_frames, int16_
 // workgroups are a multiple k of the compute units (so that equal ranges
 // fill whole rounds), with k the smallest that keeps every range no longer
 // than the shortest item: a range then touches at most two items, which is
-// all the kernel handles.
+// all the kernel handles.  With rounds (kv_splits = -2), when every item
+// has the same length and there are more items than compute units, the
+// first F whole rounds of items run instead as whole-item ranges (no
+// partials; the compute units of an XCD walk consecutive query tiles of a
+// head side by side and share its K/V in L2) and only the items left over
+// are cut into equal ranges: on the 720p layer 3.1x instead of 10.7x the
+// algorithmic HBM bytes, but 1-2% slower (measured), so the automatic
+// choice keeps the equal cut.
 constexpr int64_t kMaxLeanRounds = 16;
+constexpr double kSegmentCost = 7.0;  // fixed cost of a segment, in tile-times (Q loads, pipeline fill, drain)
 struct LeanPlan {
   int64_t units;
   int ctas;
+  int v0 = 0;       // whole-item ranges (0: every range is cut equally)
+  int64_t u0 = 0;   // units of those items
+  int round = 0;    // workgroups per round of whole-item ranges
+  double cost = 0;  // modeled time in tile-times, without the merge
 };
-LeanPlan lean_plan(const scv_cache* c, int32_t n_frames, const int16_t* units) {
+LeanPlan lean_plan(const scv_cache* c, int32_t n_frames, const int16_t* units, bool rounds = false) {
   const int rows = scv::kAttnRowsBf16;
   const int64_t nq = int64_t(n_frames) * c->g.P;
   const int64_t rows_per_chunk = std::min<int64_t>(int64_t(c->g.C) * c->g.P, nq);
   const int nch = (n_frames + c->g.C - 1) / c->g.C;
-  int64_t total = 0, shortest = INT64_MAX;
+  int64_t total = 0, shortest = INT64_MAX, longest = 0, n_items = 0;
   for (int b = 0; b < c->g.B; ++b)
     for (int ch = 0; ch < nch; ++ch) {
       const int64_t rows_ch = std::min<int64_t>(rows_per_chunk, nq - int64_t(ch) * rows_per_chunk);
       const int64_t u = units[ch + nch * b];
-      total += ((rows_ch + rows - 1) / rows) * c->g.H * u;
+      const int64_t items = ((rows_ch + rows - 1) / rows) * c->g.H;
+      total += items * u;
+      n_items += items;
       shortest = std::min(shortest, u);
+      longest = std::max(longest, u);
     }
   const int64_t cus = device_cu_count();
   const int64_t k = std::max<int64_t>(1, (total + cus * shortest - 1) / (cus * shortest));
   LeanPlan p;
   p.units = total;
   p.ctas = k <= kMaxLeanRounds ? int(k * cus) : 0;  // 0: items too short for the balanced schedule
+  if (p.ctas > 0) p.cost = double(k) * (std::ceil(double(total) / p.ctas) + 2.0 * kSegmentCost);
+  const int64_t full = n_items / cus;
+  if (rounds && shortest == longest && full >= 1 && n_items > full * cus) {
+    // whole-item rounds, then the left-over items cut equally
+    LeanPlan h;
+    h.units = total;
+    h.v0 = int(full * cus);
+    h.u0 = int64_t(h.v0) * shortest;
+    h.round = int(cus);
+    const int64_t tail = total - h.u0;
+    const int64_t kt = std::max<int64_t>(1, (tail + cus * shortest - 1) / (cus * shortest));
+    if (kt <= kMaxLeanRounds) {
+      h.ctas = int(h.v0 + kt * cus);
+      h.cost = double(full) * (double(shortest) + kSegmentCost) +
+               double(kt) * (std::ceil(double(tail) / (kt * cus)) + 2.0 * kSegmentCost);
+      p = h;
+    }
+  }
   return p;
 }
 
@@ -346,6 +379,10 @@ int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int3
   }
   const bool lean_ok = plan.ctas > 0;
   if (requested == -1) return lean_ok ? -1 : 1;
+  if (requested == -2) {
+    if (!lean_ok) return 1;
+    return lean_plan(c, n_frames, units, true).v0 > 0 ? -2 : -1;
+  }
   const int rows = scv::attn_rows_per_workgroup(c->g);
   const int64_t nq = int64_t(n_frames) * c->g.P;
   const int64_t rows_per_chunk = std::min<int64_t>(int64_t(c->g.C) * c->g.P, nq);
@@ -385,12 +422,9 @@ int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int3
   }
   if (lean_ok) {
     const LeanPlan& p = plan;
-    const double rounds = double(p.ctas / cus);
-    const double per = std::ceil(double(p.units) / p.ctas);
-    const double partial_bytes = 4.0 * p.ctas * rows * (4.0 * c->g.D + 4.0);
-    // a segment's fixed cost (Q loads, pipeline fill and drain, partial
-    // write) measured at ~7 tile-times
-    const double cost = rounds * (per + 2.0 * 7.0) + 2.0 + partial_bytes / 8.5e6;
+    // the cut ranges' partials are written and read back by the merge
+    const double partial_bytes = 4.0 * (p.ctas - p.v0) * rows * (4.0 * c->g.D + 4.0);
+    const double cost = p.cost + 2.0 + partial_bytes / 8.5e6;
     // Only a clear win moves off the grid schedule: with every compute unit
     // busy the shader clock drops a few percent (measured ~3% on the 480p
     // layer, which then runs no faster balanced), and the balanced
@@ -401,14 +435,14 @@ int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int3
 }
 
 // Workgroups of the balanced schedule (t0 null: the steady state).
-int lean_ctas(const scv_cache* c, const int64_t* t0, int32_t n_frames) {
+int lean_ctas(const scv_cache* c, const int64_t* t0, int32_t n_frames, bool rounds) {
   int16_t units[scv::kMaxBatch * scv::kMaxQueryChunks];
   class_units(c, t0, n_frames, units);
-  return lean_plan(c, n_frames, units).ctas;
+  return lean_plan(c, n_frames, units, rounds).ctas;
 }
 
 size_t workspace_bytes(const scv_cache* c, int32_t n_frames, int splits) {
-  if (splits < 0) return lean_workspace_bytes(c, lean_ctas(c, nullptr, n_frames));
+  if (splits < 0) return lean_workspace_bytes(c, lean_ctas(c, nullptr, n_frames, splits == -2));
   if (splits <= 1) return 0;
   const size_t rows = size_t(c->g.B) * c->g.H * size_t(n_frames) * c->g.P;
   return align_up(size_t(splits) * rows * c->g.D * 4, 256) + align_up(size_t(splits) * rows * 4, 256);
@@ -742,7 +776,7 @@ scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, con
 int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int32_t kv_splits,
                              size_t ws_bytes) {
   try {
-    if (!c || n_frames < 1 || kv_splits < -1) return 0;
+    if (!c || n_frames < 1 || kv_splits < -2) return 0;
     if (t0 && check_times(c, t0, n_frames) != SCV_OK) return 0;
     return resolve_splits(c, t0, n_frames, kv_splits, ws_bytes);
   } catch (...) {
@@ -752,7 +786,7 @@ int32_t scv_attention_splits(const scv_cache* c, const int64_t* t0, int32_t n_fr
 
 size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32_t kv_splits) {
   try {
-    if (!c || n_frames < 1 || kv_splits < -1) return 0;
+    if (!c || n_frames < 1 || kv_splits < -2) return 0;
     return workspace_bytes(c, n_frames, resolve_splits(c, nullptr, n_frames, kv_splits, SIZE_MAX));
   } catch (...) {
     return 0;
@@ -762,11 +796,11 @@ size_t scv_attention_workspace_bytes(const scv_cache* c, int32_t n_frames, int32
 size_t scv_attention_request_workspace_bytes(const scv_cache* c, const int64_t* t0, int32_t n_frames,
                                              int32_t kv_splits) {
   try {
-    if (!c || !t0 || n_frames < 1 || kv_splits < -1) return 0;
+    if (!c || !t0 || n_frames < 1 || kv_splits < -2) return 0;
     if (check_times(c, t0, n_frames) != SCV_OK) return 0;
     const int splits = resolve_splits(c, t0, n_frames, kv_splits, SIZE_MAX);
     if (splits >= 0) return workspace_bytes(c, n_frames, splits);
-    return lean_workspace_bytes(c, lean_ctas(c, t0, n_frames));
+    return lean_workspace_bytes(c, lean_ctas(c, t0, n_frames, splits == -2));
   } catch (...) {
     return 0;
   }
@@ -798,7 +832,7 @@ scv_status chunk_attention_impl(const scv_cache* c, const void* q_rot, const int
     if ((s = check_ptr(lse, "lse", false)) != SCV_OK) return s;
     if (n_frames < 1 || n_frames > c->g.k_max * c->g.C)
       return fail(SCV_E_SHAPE, "n_frames must be in [1, max_query_chunks*chunk_frames]");
-    if (kv_splits < -1) return fail(SCV_E_INVALID, "kv_splits must be >= -1");
+    if (kv_splits < -2) return fail(SCV_E_INVALID, "kv_splits must be >= -2");
     if ((s = check_times(c, t0, n_frames)) != SCV_OK) return s;
     // with kv_splits = 0 the choice sees t0 and the workspace given
     const int splits = resolve_splits(c, t0, n_frames, kv_splits, ws ? ws_bytes : 0);
@@ -806,7 +840,7 @@ scv_status chunk_attention_impl(const scv_cache* c, const void* q_rot, const int
     LeanPlan plan{0, 0};
     if (splits < 0) {
       class_units(c, t0, n_frames, lean_units);
-      plan = lean_plan(c, n_frames, lean_units);
+      plan = lean_plan(c, n_frames, lean_units, splits == -2);
     }
     const size_t need = splits < 0 ? lean_workspace_bytes(c, plan.ctas) : workspace_bytes(c, n_frames, splits);
     if (need > 0 && from_scratch && need > ws_bytes)
@@ -867,6 +901,9 @@ scv_status chunk_attention_impl(const scv_cache* c, const void* q_rot, const int
       a.lean = 1;
       a.lean_ctas = plan.ctas;
       a.lean_units = plan.units;
+      a.lean_v0 = plan.v0;
+      a.lean_u0 = plan.u0;
+      a.lean_round = plan.round;
       a.part_o = static_cast<float*>(ws);
       a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                             align_up(size_t(plan.ctas) * 2 * scv::kAttnRowsBf16 * c->g.D * 4, 256));

@@ -123,9 +123,16 @@ struct AttnArgs {
   // An item cut by a range boundary leaves normalised fp32 partials in
   // part_o / part_lse at [v][slot][row] (slot 0: the workgroup's first item,
   // 1: its last) for attn_lean_merge_kernel.
+  // With lean_v0 > 0 the first lean_v0 ranges are whole items instead (range
+  // v = item v, run in rounds of lean_round workgroups), and only the units
+  // [lean_u0, lean_units) of the remaining items are cut into the
+  // lean_ctas - lean_v0 equal ranges.
   int32_t lean;
   int32_t lean_ctas;
   int64_t lean_units;
+  int32_t lean_v0;
+  int32_t lean_round;
+  int64_t lean_u0;
   int16_t cls_units[kMaxBatch * kMaxQueryChunks];
 };
 

@@ -182,7 +182,7 @@ def test_attention_validation(lib):
     assert lib.scv_chunk_attention(h, q, t0(1000), 0, q, None, 1, None, 0, None) == -2
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, None, None, 1, None, 0, None) == -1
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, q + 4, 1, None, 0, None) == -4
-    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -2, None, 0, None) == -1
+    assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -3, None, 0, None) == -1
     # the balanced schedule needs its workspace
     assert lib.scv_chunk_attention(h, q, t0(1000), 3, q, None, -1, None, 0, None) == -7
     need = lib.scv_attention_workspace_bytes(h, 3, 4)
@@ -260,7 +260,12 @@ def test_auto_splits_respect_workspace_and_t0(lib):
     assert lib.scv_attention_splits(h, None, 3, 0, 0) == 1
     assert lib.scv_attention_splits(h, t0(20000), 3, 0, big) == s_steady
     assert lib.scv_attention_splits(h, t0(-1), 3, 0, big) == 0
-    assert lib.scv_attention_splits(h, t0(20000), 3, -2, big) == 0
+    assert lib.scv_attention_splits(h, t0(20000), 3, -3, big) == 0
+    # whole-item rounds on request: 516 items = 2 rounds of 256 whole items
+    # + 4 items cut into 256 ranges, 768 workgroups as for the equal cut
+    assert lib.scv_attention_splits(h, t0(20000), 3, -2, big) == -2
+    assert lib.scv_attention_request_workspace_bytes(h, t0(20000), 3, -2) == lean_ws(768)
+    assert lib.scv_attention_workspace_bytes(h, 3, -2) == lean_ws(768)
     lean = lib.scv_attention_workspace_bytes(h, 3, -1)
     assert lean > 0
     assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean) == -1
@@ -283,6 +288,7 @@ def test_balanced_schedule_plan(lib):
     cfg, h = make_handle(lib)
     assert lib.scv_attention_splits(h, t0(1000), 3, 0, big) == 1
     assert lib.scv_attention_splits(h, t0(1000), 3, -1, big) == -1
+    assert lib.scv_attention_splits(h, t0(1000), 3, -2, big) == -1  # fewer items than compute units
     assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, 0) == 0
     assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, -1) == lean_ws(256)
     assert lib.scv_attention_workspace_bytes(h, 3, -1) == lean_ws(256)

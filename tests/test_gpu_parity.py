@@ -238,6 +238,31 @@ def test_balanced_workloads(w, gpu_lib):
     check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, w.seed, n_random=48))
 
 
+ROUNDS = [
+    # 16 heads x 17 query tiles = 272 equal items: one round of whole query
+    # tiles, then 16 items cut into 256 ranges
+    small("rounds-272-items", heads=16, head_dim=64, split=(24, 20, 20), grid_h=40, grid_w=52, chunk_frames=2,
+          window_frames=2, t0=(57,), seed=143),
+    W.WAN13B_720P,
+]
+
+
+@pytest.mark.parametrize("w", ROUNDS, ids=lambda w: w.name)
+def test_rounds_schedule(w, gpu_lib):
+    """The balanced schedule with whole-item rounds (kv_splits = -2) against
+    the oracle on sampled rows, and against the equal cut."""
+    say(f"case rounds {w.name}")
+    r = run_gpu(w, kv_splits=-2)
+    assert r.splits == -2
+    oc, q_rot = oracle_replay(w)
+    check_attention(r, oc, q_rot, w, rows=sample_rows(w.query_rows, w.seed, n_random=64))
+    r1 = run_gpu(w, kv_splits=-1)
+    o1 = to_np(r1.o)
+    d = np.max(np.abs(to_np(r.o) - o1))
+    say(f"  rounds vs equal cut max-abs {d:.3e}")
+    assert d <= 2.0 ** -7 * max(1.0, float(np.max(np.abs(o1))))
+
+
 LIMITS = [
     # 64 frame slots (sink 1 + window 60 + chunk 3), the most the cache
     # accepts: slot masks and ballots use every bit; one stream wraps the
