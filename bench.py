@@ -289,8 +289,9 @@ def cold_step_ms(r, reps=5, flush_bytes=512 << 20):
 
 def ablations(w):
     """Before/after timings of design choices that can be switched from the
-    API: fused rope3d_append vs rope3d_apply + kv_append_roll, and key
-    splits.  One JSON line."""
+    API: fused rope3d_append vs rope3d_apply + kv_append_roll, and every
+    attention schedule (key splits 1/2/4/8, balanced, whole-item rounds)
+    against the host model's own choice.  One JSON line."""
     import torch
 
     from streaming_causal_video_amd.runner import StreamRunner
@@ -325,11 +326,30 @@ def ablations(w):
 
     out["append_fused_ms"] = timed(r.append)
     out["append_unfused_ms"] = timed(unfused) - timed(copies)
-    for sp in (-1, 1, 2, 4, 8):
+    # every schedule the host can pick, the one its model picks for this
+    # request (kv_splits = 0), and how far that one is from the fastest
+    names = {-2: "rounds", -1: "balanced"}
+    sched = {}
+    for sp in (1, 2, 4, 8, -1, -2):
         rs = StreamRunner(w, kv_splits=sp)
+        if rs.splits != sp:  # falls back where the schedule does not apply
+            continue
         rs.fill()
         rs.step()
-        out["attn_ms_balanced" if sp < 0 else f"attn_ms_splits_{sp}"] = timed(rs.attend)
+        sched[names.get(sp, f"splits_{sp}")] = timed(rs.attend)
+        del rs
+    auto = StreamRunner(w, kv_splits=0).splits
+    auto_name = names.get(auto, f"splits_{auto}")
+    if auto_name not in sched:
+        ra = StreamRunner(w, kv_splits=auto)
+        ra.fill()
+        ra.step()
+        sched[auto_name] = timed(ra.attend)
+    best = min(sched, key=sched.get)
+    out["attn_ms_by_schedule"] = sched
+    out["model_choice"] = auto_name
+    out["fastest"] = best
+    out["model_choice_vs_fastest"] = sched[auto_name] / sched[best] - 1.0
     print(json.dumps(out), flush=True)
 
 

@@ -257,13 +257,14 @@ scv_status scv_rope3d_append_sink(scv_cache* c, const void* q, void* q_rot, cons
  * per workgroup, with the compute units of an XCD on consecutive query
  * tiles of a head so that they share its keys and values in L2, and only
  * the query tiles left over are cut into equal ranges -- far less HBM
- * traffic (the 720p layer: 3.1x instead of 10.7x the algorithmic bytes) for
- * 1-2% more time, so kv_splits = 0 never picks it; where it does not apply
- * it falls back to -1.
+ * traffic (the 720p layer: 3.1x instead of 10.7x the algorithmic bytes) in
+ * about the same time; kv_splits = 0 picks it where the model finds it
+ * cheaper than the equal cut, and a request for it falls back to -1 where
+ * it does not apply.
  * kv_splits > 0 asks for that many splits (capped at 64 and at the number
  * of 64-key tiles); kv_splits = -1 asks for the balanced schedule (the fp32
  * path, and tiles too short for it, fall back to one split).  kv_splits = 0
- * lets a makespan model choose among both from the device's compute-unit
+ * lets a makespan model choose among all of them from the device's compute-unit
  * count: with t0 (HOST int64[batch], nullable) it counts the key tiles each
  * stream's chunks visit; with t0 = NULL it assumes every chunk sees sink +
  * window + chunk (the steady state).  Only schedules whose workspace fits

@@ -1332,7 +1332,9 @@ __global__ __launch_bounds__(256) void attn_lean_merge_kernel(AttnArgs a) {
   constexpr int TPR = 256 / kMergeRows;  // threads per row
   constexpr int NV = D / 4 / TPR;        // float4 per thread
   const Geometry& g = a.g;
-  const LeanItem it = lean_item_by_index<kRowsBf16>(a, blockIdx.x);
+  // items of whole-item ranges were written by the attention kernel: the
+  // grid starts at the first item after them
+  const LeanItem it = lean_item_by_index<kRowsBf16>(a, a.lean_v0 + int(blockIdx.x));
   const int c_first = lean_range_of(a, it.start);
   const int c_last = lean_range_of(a, it.start + it.units - 1);
   if (c_first == c_last) return;
@@ -1342,6 +1344,7 @@ __global__ __launch_bounds__(256) void attn_lean_merge_kernel(AttnArgs a) {
   const bool rvalid = r < qt.row_end - qt.row_lo;
   const int j0 = threadIdx.x % TPR;
   __shared__ int64_t part[64];
+  __shared__ int64_t starts[65];
   __shared__ int n_part;
   const int first_slot = it.start == lean_range_start(a, c_first) ? 0 : 1;
   float m = -INFINITY, sum = 0.f;
@@ -1350,38 +1353,59 @@ __global__ __launch_bounds__(256) void attn_lean_merge_kernel(AttnArgs a) {
   for (int v = 0; v < NV; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = c_first; c0 <= c_last; c0 += 64) {
     __syncthreads();
+    // the starts of ranges c0 .. c0 + 64, one per thread, then the list
+    const int nc = min(c_last, c0 + 63) - c0 + 1;
+    if (int(threadIdx.x) <= nc) starts[threadIdx.x] = lean_range_start(a, c0 + int(threadIdx.x));
+    __syncthreads();
     if (threadIdx.x == 0) {
       int n = 0;
-      int64_t lo = lean_range_start(a, c0);
-      for (int c = c0; c <= min(c_last, c0 + 63); ++c) {
-        const int64_t hi = lean_range_start(a, c + 1);
-        if (hi > lo) part[n++] = (int64_t(c) * 2 + (c == c_first ? first_slot : 0)) * kRowsBf16;  // ranges with no unit wrote nothing
-        lo = hi;
+      for (int i = 0; i < nc; ++i) {
+        const int c = c0 + i;
+        if (starts[i + 1] > starts[i])  // ranges with no unit wrote nothing
+          part[n++] = (int64_t(c) * 2 + (c == c_first ? first_slot : 0)) * kRowsBf16;
       }
       n_part = n;
     }
     __syncthreads();
     if (!rvalid) continue;
     const int n = n_part;
-    for (int k = 0; k < n; ++k) {
-      const int64_t pr = part[k] + r;
-      const float l = a.part_lse[pr];
-      float4 x[NV];
+    // partials in batches of kMergeBatch: every load of a batch is issued
+    // before any is used (an item cut into many ranges, as the left-over
+    // items of whole-item rounds are, would otherwise wait one memory
+    // latency per partial); they are combined in the same order as one by one
+    constexpr int kMergeBatch = 4;
+    for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
+      float lb[kMergeBatch];
+      float4 xb[kMergeBatch][NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) x[v] = *reinterpret_cast<const float4*>(a.part_o + pr * D + 4 * (j0 + TPR * v));
-      if (l == -INFINITY) continue;
-      const float m_new = fmaxf(m, l);
-      const float sc = __expf(m - m_new);  // 0 while m is -inf
-      const float w = __expf(l - m_new);
-      sum = sum * sc + w;
+      for (int kk = 0; kk < kMergeBatch; ++kk) {
+        lb[kk] = -INFINITY;
+        if (k0 + kk < n) {
+          const int64_t pr = part[k0 + kk] + r;
+          lb[kk] = a.part_lse[pr];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        acc[v].x = acc[v].x * sc + w * x[v].x;
-        acc[v].y = acc[v].y * sc + w * x[v].y;
-        acc[v].z = acc[v].z * sc + w * x[v].z;
-        acc[v].w = acc[v].w * sc + w * x[v].w;
+          for (int v = 0; v < NV; ++v)
+            xb[kk][v] = *reinterpret_cast<const float4*>(a.part_o + pr * D + 4 * (j0 + TPR * v));
+        }
       }
-      m = m_new;
+#pragma unroll
+      for (int kk = 0; kk < kMergeBatch; ++kk) {
+        const float l = lb[kk];
+        if (l == -INFINITY) continue;
+        const float4* x = xb[kk];
+        const float m_new = fmaxf(m, l);
+        const float sc = __expf(m - m_new);  // 0 while m is -inf
+        const float w = __expf(l - m_new);
+        sum = sum * sc + w;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          acc[v].x = acc[v].x * sc + w * x[v].x;
+          acc[v].y = acc[v].y * sc + w * x[v].y;
+          acc[v].z = acc[v].z * sc + w * x[v].z;
+          acc[v].w = acc[v].w * sc + w * x[v].w;
+        }
+        m = m_new;
+      }
     }
   }
   if (!rvalid) return;
@@ -1407,7 +1431,7 @@ hipError_t launch_attn_lean_merge(const AttnArgs& a, hipStream_t s) {
   int per_head = 0;
   for (int ch = 0; ch < nch; ++ch)
     per_head += (std::min(a.rows_per_chunk, a.Nq - ch * a.rows_per_chunk) + kRowsBf16 - 1) / kRowsBf16;
-  dim3 grid(unsigned(per_head * a.g.H * a.g.B), kRowsBf16 / kMergeRows);
+  dim3 grid(unsigned(per_head * a.g.H * a.g.B - a.lean_v0), kRowsBf16 / kMergeRows);
   if (a.g.D == 128)
     hipLaunchKernelGGL(attn_lean_merge_kernel<128>, grid, dim3(256), 0, s, a);
   else

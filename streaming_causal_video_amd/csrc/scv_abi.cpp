@@ -300,8 +300,10 @@ void class_units(const scv_cache* c, const int64_t* t0, int32_t n_frames, int16_
 // partials; the compute units of an XCD walk consecutive query tiles of a
 // head side by side and share its K/V in L2) and only the items left over
 // are cut into equal ranges: on the 720p layer 3.1x instead of 10.7x the
-// algorithmic HBM bytes, but 1-2% slower (measured), so the automatic
-// choice keeps the equal cut.
+// algorithmic HBM bytes, and the same time within the spread between
+// boxes (A/B on four boxes: -1.9% to +1.8%, +0.1% on average).  The
+// automatic choice takes whichever cut the model finds cheaper (rounds
+// write fewer partials).
 constexpr int64_t kMaxLeanRounds = 16;
 constexpr double kSegmentCost = 7.0;  // fixed cost of a segment, in tile-times (Q loads, pipeline fill, drain)
 struct LeanPlan {
@@ -421,15 +423,24 @@ int resolve_splits(const scv_cache* c, const int64_t* t0, int32_t n_frames, int3
     }
   }
   if (lean_ok) {
-    const LeanPlan& p = plan;
     // the cut ranges' partials are written and read back by the merge
-    const double partial_bytes = 4.0 * (p.ctas - p.v0) * rows * (4.0 * c->g.D + 4.0);
-    const double cost = p.cost + 2.0 + partial_bytes / 8.5e6;
+    auto lean_cost = [&](const LeanPlan& p) {
+      const double partial_bytes = 4.0 * (p.ctas - p.v0) * rows * (4.0 * c->g.D + 4.0);
+      return p.cost + 2.0 + partial_bytes / 8.5e6;
+    };
+    int lean_s = -1;
+    double cost = lean_cost(plan);
+    const LeanPlan pr = lean_plan(c, n_frames, units, true);
+    if (pr.v0 > 0 && lean_cost(pr) < cost && lean_workspace_bytes(c, pr.ctas) <= ws_limit) {
+      lean_s = -2;
+      cost = lean_cost(pr);
+    }
     // Only a clear win moves off the grid schedule: with every compute unit
     // busy the shader clock drops a few percent (measured ~3% on the 480p
     // layer, which then runs no faster balanced), and the balanced
     // schedule reads more K/V from HBM.
-    if (cost < 0.95 * best && lean_workspace_bytes(c, p.ctas) <= ws_limit) return -1;
+    const int ctas = lean_s == -2 ? pr.ctas : plan.ctas;
+    if (cost < 0.95 * best && lean_workspace_bytes(c, ctas) <= ws_limit) return lean_s;
   }
   return best_s;
 }

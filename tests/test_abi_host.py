@@ -249,13 +249,13 @@ def test_sink_update_validation(lib):
 
 
 def test_auto_splits_respect_workspace_and_t0(lib):
-    # 720p, one stream: the steady-state choice is the balanced schedule;
-    # without workspace it runs unsplit; with only a split-sized workspace
-    # it splits
+    # 720p, one stream: the steady-state choice is the balanced schedule with
+    # whole-item rounds (fewer partials than the equal cut); without
+    # workspace it runs unsplit; with only a split-sized workspace it splits
     cfg, h = make_handle(lib, grid_h=45, grid_w=80, window_frames=8)
     big = (1 << 64) - 1
     s_steady = lib.scv_attention_splits(h, None, 3, 0, big)
-    assert s_steady == -1
+    assert s_steady == -2
     assert lib.scv_attention_workspace_bytes(h, 3, 0) > 0
     assert lib.scv_attention_splits(h, None, 3, 0, 0) == 1
     assert lib.scv_attention_splits(h, t0(20000), 3, 0, big) == s_steady
@@ -268,7 +268,7 @@ def test_auto_splits_respect_workspace_and_t0(lib):
     assert lib.scv_attention_workspace_bytes(h, 3, -2) == lean_ws(768)
     lean = lib.scv_attention_workspace_bytes(h, 3, -1)
     assert lean > 0
-    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean) == -1
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean) == -2  # same 768 workgroups
     assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean - 1) > 1  # key splits that fit
     lib.scv_cache_destroy(h)
 

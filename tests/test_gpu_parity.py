@@ -263,6 +263,36 @@ def test_rounds_schedule(w, gpu_lib):
     assert d <= 2.0 ** -7 * max(1.0, float(np.max(np.abs(o1))))
 
 
+def test_side_stream_workspace(gpu_lib):
+    """chunk_attention on a side stream with a workspace the binding
+    allocates itself, while the default stream allocates and overwrites
+    memory right after the call returns: the output equals the default
+    stream's (the workspace stays reserved for the side stream until its
+    kernels are done)."""
+    import torch
+
+    w = small("side-stream", heads=3, grid_h=15, grid_w=26, chunk_frames=2, window_frames=4, t0=(31,), seed=144)
+    say(f"case side stream {w.name}")
+    r = run_gpu(w, kv_splits=4)
+    assert r.splits == 4
+    o_ref, lse_ref = r.o.clone(), r.lse.clone()
+    need = r.cache.request_workspace_bytes(w.t0, r.n_frames, 4)
+    assert need > 0
+    side = torch.cuda.Stream()
+    o2, lse2 = torch.empty_like(r.o), torch.empty_like(r.lse)
+    a = torch.randn(4096, 4096, device="cuda")
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(8):  # keeps the side stream busy past the call's return
+            a = (a @ a) * 1e-3
+    r.cache.chunk_attention(r.q_rot, w.t0, r.n_frames, o2, lse2, kv_splits=4, stream=side)
+    junk = [torch.full((need // 4 + 1,), float("nan"), device="cuda") for _ in range(3)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(o2, o_ref) and torch.equal(lse2, lse_ref)
+
+
 LIMITS = [
     # 64 frame slots (sink 1 + window 60 + chunk 3), the most the cache
     # accepts: slot masks and ballots use every bit; one stream wraps the
