@@ -27,7 +27,7 @@ Sources, cited by page title and section:
   quadratic cost of full spatio-temporal attention and the causal KV cache.
 
 The pages print no formula for RoPE or attention and no worked example.
-Readings taken where they are silent (each also listed in the design doc):
+Readings taken where they are silent:
 
 * R1 pairs are adjacent (2j, 2j+1) inside each axis block (RoPE as a complex
   multiply); R2 each axis a in {t, h, w} is its own 1-D RoPE of width d_a with
