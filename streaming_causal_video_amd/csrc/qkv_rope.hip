@@ -45,6 +45,8 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kQK = 64;        // reduction depth of one LDS slice
 constexpr int kQTokGroups = 4; // waves per feature block
+constexpr int kBand = 6;       // token tiles per band of the workgroup order
+constexpr int kSpread = 8;     // MFMA groups over which a slice's loads are issued
 
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(voff), "s"(base) : "m0", "memory");
@@ -62,19 +64,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// byte offset of 16-byte chunk c of row r in a slice (64-byte rows)
+// byte offset of 16-byte chunk c of row r in a slice (128-byte rows)
 __device__ __forceinline__ int slice_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // fp32 -> T (round to nearest even).  fp16 saturates: a value beyond the
 // largest finite fp16 is stored as +-65504 instead of +-inf, so rotated keys
 // stay finite and the attention over them stays defined.
-// cos/sin of a time pair whose frame is not in the LDS table (a tile
-// spanning more frames than the table holds); out of line so that the
-// compiler never evaluates it speculatively on the common path
-__device__ __attribute__((noinline)) float2 rope_cos_sin_slow(int64_t pos, double omega) {
-  return rope_cos_sin(pos, omega);
-}
-
 template <typename T>
 __device__ __forceinline__ uint16_t bits16(float x) {
   if constexpr (std::is_same<T, _Float16>::value) x = __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f);
@@ -112,9 +107,11 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const int grp = wave / kTokGroups, wq = wave % kTokGroups;  // feature block, token group
   const int hl = lane >> 5, l32 = lane & 31;
   // Workgroups go to the 8 XCDs round robin; renumber them so that each
-  // XCD runs a contiguous range of (token tile fastest, feature pair,
-  // stream): its few feature pairs' weights stay in its L2 while the token
-  // tiles stream past.
+  // XCD runs a contiguous range of logical tiles, ordered in bands of
+  // kBand token tiles (token tile fastest within a band, then feature pair,
+  // then band, then stream): the ~32 workgroups an XCD runs at once cover a
+  // compact block of token tiles x feature pairs, whose x and weight slices
+  // its L2 serves to all of them.
   int mt, fpair, b;
   {
     const int nx = gridDim.x, ny = gridDim.y, n = nx * ny * gridDim.z;
@@ -122,9 +119,13 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
     const int xcd = id % 8, k = id / 8;
     const int base = n / 8, extra = n % 8;
     const int logical = xcd * base + min(xcd, extra) + k;
-    mt = logical % nx;
-    fpair = (logical / nx) % ny;
     b = logical / (nx * ny);
+    const int r = logical - b * (nx * ny);
+    const int band = r / (kBand * ny), first = band * kBand;
+    const int width = min(kBand, nx - first);  // the last band may be narrower
+    const int q = r - band * (kBand * ny);
+    mt = first + q % width;
+    fpair = q / width;
   }
   const int n_blocks = 3 * g.H;
   const int fb0 = 2 * fpair;
@@ -137,122 +138,148 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const int f_lo = m0 / g.P;
   const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
 
-  // ---- global -> LDS slices (source offsets are loop invariant) ----
+  // ---- global -> LDS slices ----
+  // Piece (wave * X_DMA + j) * 64 + lane of a stage's x part is 16-byte
+  // chunk c of row r = piece / 8, stored at chunk position
+  // (lane % 8) = c ^ ((r / 2) % 8), so c = c0 ^ (4 * (piece / 64 % 2)) with
+  // c0 = (lane % 8) ^ (lane / 16); the weight part likewise.  Offsets are
+  // recomputed for every slice from two lane values, which keeps ten
+  // registers free for the fragment pipeline below.
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
-  const char* xbase = static_cast<const char*>(a.x) + int64_t(b) * Ntok * Dm * 2;
-  const char* wbase = static_cast<const char*>(a.w) + int64_t(fb0) * D * Dm * 2;
+  const char* const xs = uniform_ptr(static_cast<const char*>(a.x) + int64_t(b) * Ntok * Dm * 2);
+  const char* const ws = uniform_ptr(static_cast<const char*>(a.w) + int64_t(fb0) * D * Dm * 2);
   const int w_rows = min(2, n_blocks - fb0) * D;  // weight rows that exist
-  // hi: bit j set where load j of this lane fetches a chunk of the second
-  // half of the 128-byte row piece (moved back by 64 bytes in a final
-  // 32-deep slice, whose second half lies past the end of the row)
-  uint32_t xo[X_DMA], wo[W_DMA], hi = 0;
-#pragma unroll
-  for (int j = 0; j < X_DMA; ++j) {
-    const int piece = (wave * X_DMA + j) * 64 + lane, r = piece >> 3, c = (piece & 7) ^ ((r >> 1) & 7);
-    const int tok = min(m0 + r, Ntok - 1);  // rows past the last token repeat it (outputs dropped)
-    xo[j] = uint32_t(tok) * uint32_t(Dm * 2) + uint32_t(c << 4);
-    hi |= uint32_t(c >> 2) << j;
-  }
-#pragma unroll
-  for (int j = 0; j < W_DMA; ++j) {
-    const int piece = (wave * W_DMA + j) * 64 + lane, r = piece >> 3, c = (piece & 7) ^ ((r >> 1) & 7);
-    const int rr = min(r, w_rows - 1);  // a missing second block repeats the last row (unused)
-    wo[j] = uint32_t(rr) * uint32_t(Dm * 2) + uint32_t(c << 4);
-    hi |= uint32_t(c >> 2) << (X_DMA + j);
-  }
   const int n_full = Dm / kQK;              // 64-deep slices
   const bool half_tail = Dm % kQK != 0;     // then one more, 32 deep
   // LDS: the x stages [2][XB], then the weight stages [2][WB], so that every
   // fragment read reaches its stage with an immediate offset below 64 KB
-  auto issue = [&](int kt, int stg) {
+  // load j (0 <= j < DMA) of this wave for slice kt into stage stg: x
+  // pieces first, then weight pieces; lrow = lane / 8 and c0 come in
+  // through an empty asm per slice
+  auto issue_one = [&](int kt, int stg, int j, int lrow, int c0) __attribute__((always_inline)) {
     const int64_t k0 = int64_t(kt) * kQK * 2;
-    const uint32_t back = kt == n_full ? hi : 0u;  // the 32-deep slice: second-half chunks repeat the first half
+    // the 32-deep slice: second-half chunks (c >= 4) repeat the first half
+    const bool tail = kt == n_full;
+    if (j < X_DMA) {
+      const int blk = wave * X_DMA + j;
+      const int c = c0 ^ ((blk & 1) << 2);
+      const int tok = min(m0 + blk * 8 + lrow, Ntok - 1);  // rows past the last token repeat it (outputs dropped)
+      const uint32_t off = uint32_t(tok) * uint32_t(Dm * 2) + uint32_t(c << 4) - (tail ? uint32_t(c >> 2) << 6 : 0u);
+      dma16(xs + k0, off, lds0 + uint32_t(stg * XB + blk * 1024));
+    } else {
+      const int blk = wave * W_DMA + (j - X_DMA);
+      const int c = c0 ^ ((blk & 1) << 2);
+      const int rr = min(blk * 8 + lrow, w_rows - 1);  // a missing second block repeats the last row (unused)
+      const uint32_t off = uint32_t(rr) * uint32_t(Dm * 2) + uint32_t(c << 4) - (tail ? uint32_t(c >> 2) << 6 : 0u);
+      dma16(ws + k0, off, lds0 + uint32_t(2 * XB + stg * WB + blk * 1024));
+    }
+  };
+  auto lane_parts = [&](int& lrow, int& c0) __attribute__((always_inline)) {
+    lrow = lane >> 3;
+    c0 = (lane & 7) ^ (lane >> 4);
+    asm volatile("" : "+v"(lrow));
+    asm volatile("" : "+v"(c0));
+  };
+  auto issue = [&](int kt, int stg) __attribute__((always_inline)) {
+    int lrow, c0;
+    lane_parts(lrow, c0);
 #pragma unroll
-    for (int j = 0; j < X_DMA; ++j)
-      dma16(uniform_ptr(xbase + k0), xo[j] - (((back >> j) & 1u) << 6),
-            lds0 + uint32_t(stg * XB + (wave * X_DMA + j) * 1024));
-#pragma unroll
-    for (int j = 0; j < W_DMA; ++j)
-      dma16(uniform_ptr(wbase + k0), wo[j] - (((back >> (X_DMA + j)) & 1u) << 6),
-            lds0 + uint32_t(2 * XB + stg * WB + (wave * W_DMA + j) * 1024));
+    for (int j = 0; j < DMA; ++j) issue_one(kt, stg, j, lrow, c0);
   };
 
   floatx16_t acc[DB * TB];
 #pragma unroll
   for (int i = 0; i < DB * TB; ++i) acc[i] = floatx16_t{};
 
-  // this lane's fragment offsets in stage 0 (chunk 2*kk + hl of the row); a
-  // 32-row block adds 4096 bytes, a stage XB or WB
-  int xoff[4], woff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    xoff[kk] = slice_off(32 * TB * wq + l32, 2 * kk + hl);
-    woff[kk] = 2 * XB + slice_off(D * grp + l32, 2 * kk + hl);
-  }
+  // this lane's fragment offsets in stage 0 for step kk = 0 (chunk hl of its
+  // row); step kk reads chunk 2*kk + hl, at offset ^ (kk * 32) since the
+  // swizzle is an XOR; a 32-row block adds 4096 bytes, a stage XB or WB
+  int xoff = slice_off(32 * TB * wq + l32, hl);
+  int woff = 2 * XB + slice_off(D * grp + l32, hl);
 
-  // Every wave passes the same barriers; the MFMA operand order (C^T for q
-  // and k, C for v) is per wave.  A wave reads the fragments of a 16-deep
-  // step and then runs its MFMAs; the SIMD's other wave covers the wait.
-  struct Frags {
-    bf16x8_t x[TB], w[DB];
-  };
-  auto read = [&](int stg, int kk, Frags& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      f.x[tb] = *reinterpret_cast<const bf16x8_t*>(smem + xoff[kk] + stg * XB + tb * 4096);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      f.w[db] = *reinterpret_cast<const bf16x8_t*>(smem + woff[kk] + stg * WB + db * 4096);
-  };
+  // Fragment pipeline: a wave's 16-deep step is DB groups of TB MFMAs, one
+  // group per weight fragment.  The read of the next group's weight
+  // fragment (and, in the last group, of the next step's x fragments) is
+  // issued before the current group's MFMAs, so its LDS latency hides
+  // behind them instead of stalling the wave; the SIMD's other wave covers
+  // what is left.  Every wave passes the same barriers; the MFMA operand
+  // order (C^T for q and k, C for v) is per wave.
   auto gemm = [&](auto trans_tag) {
     constexpr bool kTrans = decltype(trans_tag)::value;  // C^T: features as rows
-    auto mma = [&](const Frags& f) {
+    auto group = [&](const bf16x8_t (&x)[TB], const bf16x8_t& w, int db) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          if constexpr (kTrans)
-            acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[db], f.x[tb], acc[db * TB + tb], 0, 0, 0);
-          else
-            acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[tb], f.w[db], acc[db * TB + tb], 0, 0, 0);
-        }
+      for (int tb = 0; tb < TB; ++tb) {
+        if constexpr (kTrans)
+          acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, x[tb], acc[db * TB + tb], 0, 0, 0);
+        else
+          acc[db * TB + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[tb], w, acc[db * TB + tb], 0, 0, 0);
+      }
     };
     const int n_k = n_full + (half_tail ? 1 : 0);
     // two stages: slice kt+1 loads while slice kt is computed
     issue(0, 0);
     if (n_k > 1) issue(1, 1);
-    // slice kt in stage kt % 2 (a constant: the loop is unrolled twice)
-    auto slice = [&](auto stg_c, int kt) __attribute__((always_inline)) {
-      constexpr int stg = decltype(stg_c)::value;
-      // the offsets pass through an empty asm each slice, so that offset +
-      // stage is formed at the read (as its immediate) instead of being
-      // hoisted out of the loop into registers
+    // slice kt (in stage kt % 2) with NKK 16-deep steps: one instance for
+    // the 64-deep slices, one for a 32-deep tail
+    auto slice = [&](auto nkk_c, int kt) __attribute__((always_inline)) {
+      constexpr int NKK = decltype(nkk_c)::value;
+      const int stg = kt & 1;
+      // the offsets pass through an empty asm each slice, so that the step
+      // offsets are formed anew (one XOR each; stages and blocks are
+      // multiples of 1 KB, which the XOR leaves alone) and block offsets
+      // become read immediates, instead of all being hoisted out of the
+      // loop into registers
+      int xo = xoff + stg * XB, wo = woff + stg * WB;
+      asm volatile("" : "+v"(xo));
+      asm volatile("" : "+v"(wo));
+      auto read_x = [&](int kk, bf16x8_t (&x)[TB]) __attribute__((always_inline)) {
+        const int o = xo ^ (kk << 5);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        asm volatile("" : "+v"(xoff[kk]));
-        asm volatile("" : "+v"(woff[kk]));
-      }
+        for (int tb = 0; tb < TB; ++tb) x[tb] = *reinterpret_cast<const bf16x8_t*>(smem + o + tb * 4096);
+      };
+      auto read_w = [&](int kk, int db) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8_t*>(smem + (wo ^ (kk << 5)) + db * 4096);
+      };
       if (kt == 0 && n_k > 1)
         wait_vm<DMA>();
       else
         wait_vm<0>();
       __syncthreads();  // slice kt landed everywhere; slice kt-1 is done everywhere
-      if (kt >= 1 && kt + 1 < n_k) issue(kt + 1, stg ^ 1);
-      const int n_kk = kt == n_full ? 2 : 4;  // 16-deep steps in this slice
+      // slice kt+1's loads (into the stage slice kt-1 used) are spread over
+      // the first kSpread groups, so that a wave never stalls on issuing
+      // them all at once behind the other waves' loads
+      const bool load_next = kt >= 1 && kt + 1 < n_k;
+      int lrow = 0, c0 = 0;
+      if (load_next) lane_parts(lrow, c0);
+      bf16x8_t x[2][TB], w[2];
+      read_x(0, x[0]);
+      w[0] = read_w(0, 0);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk >= n_kk) break;
-        Frags f;
-        read(stg, kk, f);
-        mma(f);
-      }
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int cur = (kk * DB + db) & 1;
+          const int grp_i = kk * DB + db;
+          if (NKK == 4 && grp_i < kSpread && load_next) {
+#pragma unroll
+            for (int j = grp_i * DMA / kSpread; j < (grp_i + 1) * DMA / kSpread; ++j) issue_one(kt + 1, stg ^ 1, j, lrow, c0);
+          }
+          // the reads first, then the group's MFMAs
+          if (db + 1 < DB) {
+            w[cur ^ 1] = read_w(kk, db + 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          } else if (kk + 1 < NKK) {
+            read_x(kk + 1, x[(kk + 1) & 1]);
+            w[cur ^ 1] = read_w(kk + 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, TB + 1, 0);
+          }
+          group(x[kk & 1], w[cur], db);
+          __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    int kt = 0;
-    for (; kt + 2 <= n_k; kt += 2) {
-      slice(std::integral_constant<int, 0>{}, kt);
-      slice(std::integral_constant<int, 1>{}, kt + 1);
-    }
-    if (kt < n_k) slice(std::integral_constant<int, 0>{}, kt);
+    for (int kt = 0; kt < n_full; ++kt) slice(std::integral_constant<int, 4>{}, kt);
+    if (half_tail) slice(std::integral_constant<int, 2>{}, n_full);
   };
 
   const int64_t t0 = a.t0[b];
@@ -268,37 +295,47 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
 
   // ---- after the K loop the ring holds, from its start, the RoPE tables
   // (cos/sin of the time pairs of the frames this tile spans, computed from
-  // fp64 angles, then copies of the height and width tables) and, at its
-  // end, one staging area per wave through which the outputs leave in whole
-  // 16-byte pieces of contiguous rows ----
-  constexpr int kRing = kQStages * STAGE;
-  constexpr int kStageOut = 32 * D * 2;             // one 32-token x D block
-  constexpr int kOutBase = kRing - kQWaves * kStageOut;
-  static_assert(kOutBase >= 16384, "room for the tables");
+  // fp64 angles, then copies of the height and width tables), the ring row
+  // base of each of those frames, and, at its end, one staging area per wave
+  // through which the outputs leave in whole 16-byte pieces of contiguous
+  // rows.  The host checks that the tables fit (qkv_table_bytes). ----
+  constexpr int kStageOut = 32 * D * 2;  // one 32-token x D block
+  constexpr int kOutBase = qkv_table_capacity(D, TB);
+  static_assert(kOutBase + kQWaves * kStageOut == kQStages * STAGE, "epilogue layout");
   float2* tab = reinterpret_cast<float2*>(smem);
   char* outst = smem + kOutBase + wave * kStageOut;  // this wave's staging area
   const int dh2 = g.dh / 2, dw2 = g.dw / 2;
-  const int hw_n = g.grid_h * dh2 + g.grid_w * dw2;
   const int f_hi = (min(m0 + kQM, Ntok) - 1) / g.P;
-  constexpr int kTabCap = kOutBase / int(sizeof(float2));
-  const bool hw_lds = hw_n <= kTabCap / 2;  // else read from global memory
-  const int nf_tab = min(f_hi - f_lo + 1, (kTabCap - (hw_lds ? hw_n : 0)) / max(pt, 1));
-  const int h_base = nf_tab * pt, w_base = h_base + g.grid_h * dh2;
+  const int nf = f_hi - f_lo + 1;  // frames the tile spans
+  const int h_base = nf * pt, w_base = h_base + g.grid_h * dh2;
+  // ring row of token t of frame f (frame-relative to the call) is
+  // row_base[f - f_lo] + t
+  int* row_base = reinterpret_cast<int*>(tab + w_base + g.grid_w * dw2);
   __syncthreads();  // every wave is done with the ring
-  for (int i = tid; i < nf_tab * pt; i += kThreads) {
+  for (int i = tid; i < nf * pt; i += kThreads) {
     const int fi = i / pt, j = i - fi * pt;
     tab[i] = rope_cos_sin(t0 + f_lo + fi - a.pos_off[b], a.omega_t[j]);
   }
-  if (hw_lds) {
-    for (int i = tid; i < g.grid_h * dh2; i += kThreads) tab[h_base + i] = a.tab_h[i];
-    for (int i = tid; i < g.grid_w * dw2; i += kThreads) tab[w_base + i] = a.tab_w[i];
-  }
+  for (int i = tid; i < g.grid_h * dh2; i += kThreads) tab[h_base + i] = a.tab_h[i];
+  for (int i = tid; i < g.grid_w * dw2; i += kThreads) tab[w_base + i] = a.tab_w[i];
+  for (int i = tid; i < nf; i += kThreads)
+    row_base[i] = int(slot_of(f_lo + i) * g.slot_rows - int64_t(f_lo + i) * g.P);
   __syncthreads();
   if (!fb_valid) return;
-  // frame of token t and its ring row (slot * slot_rows + position)
-  auto ring_row = [&](int t) -> int64_t {
-    const int f = t / g.P;
-    return slot_of(f) * g.slot_rows + (t - f * g.P);
+  // t / P and p / grid_w through a float reciprocal and one correction step
+  // (exact: tokens per call stay below 2^24, so the estimate is off by at
+  // most one)
+  const float inv_p = 1.0f / float(g.P), inv_w = 1.0f / float(g.grid_w);
+  auto div_fix = [](int n, int d, float inv, int& q, int& r) __attribute__((always_inline)) {
+    q = int(float(n) * inv);
+    r = n - q * d;
+    if (r < 0) {
+      --q;
+      r += d;
+    } else if (r >= d) {
+      ++q;
+      r -= d;
+    }
   };
 
   if (sel < 2) {
@@ -313,35 +350,22 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
       const int tile0 = m0 + 32 * TB * wq + 32 * tb;  // first token of this block
       {
         const int t = min(tile0 + l32, Ntok - 1);  // rows past the last token are computed but not stored
-        const int f = t / g.P, p = t - f * g.P;
-        const int yy = p / g.grid_w, xx = p - yy * g.grid_w;
-        const int fi = f - f_lo;
-        // entry bases such that pair j's entry is base + j
-        const int tbase = fi * pt;
-        const int hbase = h_base + yy * dh2 - pt, wbase = w_base + xx * dw2 - pth;
-        const bool t_in_tab = fi < nf_tab;
+        int f, p, yy, xx;
+        div_fix(t, g.P, inv_p, f, p);
+        div_fix(p, g.grid_w, inv_w, yy, xx);
+        // table entry of pair j: j + (time, height or width base)
+        const int bt = (f - f_lo) * pt, bh = h_base + yy * dh2 - pt, bw = w_base + xx * dw2 - pth;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int d0 = 32 * db + 8 * e + 4 * hl;
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = acc[db * TB + tb][4 * e + i];
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-              const int j = d0 / 2 + pp;
-              float2 cs;
-              if (j < pt) {
-                if (t_in_tab)
-                  cs = tab[tbase + j];
-                else
-                  cs = rope_cos_sin_slow(t0 + f - a.pos_off[b], a.omega_t[j]);
-              } else if (hw_lds) {
-                cs = tab[j < pth ? hbase + j : wbase + j];
-              } else {
-                cs = j < pth ? a.tab_h[yy * dh2 + (j - pt)] : a.tab_w[xx * dw2 + (j - pth)];
-              }
+              const int j = 16 * db + 4 * e + 2 * hl + pp;
+              const float2 cs = tab[j + (j < pt ? bt : (j < pth ? bh : bw))];
               const float u = v[2 * pp], w = v[2 * pp + 1];
               v[2 * pp] = u * cs.x - w * cs.y;
               v[2 * pp + 1] = u * cs.y + w * cs.x;
@@ -361,7 +385,14 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
         const uint4 val = *reinterpret_cast<const uint4*>(outst + r * (D * 2) + ((c ^ (r % kChunks)) << 4));
         const int t = tile0 + r;
         if (t < Ntok) {
-          const int64_t row = sel == 0 ? int64_t(t) * g.H : ring_row(t);
+          int64_t row;
+          if (sel == 0) {
+            row = int64_t(t) * g.H;
+          } else {
+            int f, p;
+            div_fix(t, g.P, inv_p, f, p);
+            row = row_base[f - f_lo] + t;
+          }
           *reinterpret_cast<uint4*>(out_base + row * D + c * 8) = val;
         }
       }
@@ -388,22 +419,30 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
           const int r = 32 * db + l32;
           *reinterpret_cast<uint2*>(outst + r * 64 + ((e ^ ((r >> 2) & 3)) << 4) + hl * 8) = o;
         }
+      // this lane's 8 tokens (the same in every row it stores)
+      const int t = tile0 + 8 * (lane & 3);
+      int f, p;
+      div_fix(min(t, Ntok - 1), g.P, inv_p, f, p);
+      const bool whole = (p & 7) == 0 && p + 7 < g.P && t + 7 < Ntok;
+      const int row0 = t < Ntok ? row_base[f - f_lo] + t : 0;
       asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 #pragma unroll
       for (int n = 0; n < D * 4 / 64; ++n) {
         const int r = 16 * n + (lane >> 2), c = lane & 3;
         const uint4 val = *reinterpret_cast<const uint4*>(outst + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
-        const int t = tile0 + 8 * c;
         if (t >= Ntok) continue;
         uint16_t* vrow = vt + int64_t(r) * g.rows_pad;
-        const int f = t / g.P, p = t - f * g.P;
-        if ((p & 7) == 0 && p + 7 < g.P && t + 7 < Ntok) {
-          *reinterpret_cast<uint4*>(vrow + slot_of(f) * g.slot_rows + p) = val;
+        if (whole) {
+          *reinterpret_cast<uint4*>(vrow + row0) = val;
         } else {
           const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (t + i < Ntok) vrow[ring_row(t + i)] = uint16_t(w4[i / 2] >> (16 * (i & 1)));
+            if (t + i < Ntok) {
+              int fi, pi;
+              div_fix(t + i, g.P, inv_p, fi, pi);
+              vrow[row_base[fi - f_lo] + t + i] = uint16_t(w4[i / 2] >> (16 * (i & 1)));
+            }
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");

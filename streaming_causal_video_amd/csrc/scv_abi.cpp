@@ -751,6 +751,8 @@ scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, con
     if (3 * int64_t(c->g.H) > 65535) return fail(SCV_E_SHAPE, "the fused projection supports at most 21845 heads");
     if (int64_t(n_frames) * c->g.P * d_model * 2 >= (int64_t(1) << 31))
       return fail(SCV_E_SHAPE, "n_frames * P * d_model * 2 bytes must stay below 2^31 per stream");
+    if (int64_t(n_frames) * c->g.P >= (int64_t(1) << 24))
+      return fail(SCV_E_SHAPE, "n_frames * P must stay below 2^24 tokens per call");
     scv::QkvArgs a;
     std::memset(&a, 0, sizeof(a));
     a.x = x;
@@ -772,6 +774,14 @@ scv_status scv_qkv_rope_append(scv_cache* c, const void* x, int32_t d_model, con
       const int cus = device_cu_count();
       auto cost = [&](int64_t tile) { return ((ntok + tile - 1) / tile * pairs + cus - 1) / cus * tile; };
       a.token_tile = cost(384) < cost(256) ? 384 : 256;
+      // the epilogue keeps its RoPE tables in LDS; 384-token tiles leave
+      // more room for them
+      const int D = c->g.D;
+      auto fits = [&](int tile) { return scv::qkv_table_bytes(c->g, tile) <= scv::qkv_table_capacity(D, tile / 128); };
+      if (!fits(a.token_tile)) a.token_tile = 384;
+      if (!fits(a.token_tile))
+        return fail(SCV_E_SHAPE, "the fused projection's RoPE tables (frames per tile x dt/2 + grid_h x dh/2 + "
+                                 "grid_w x dw/2 pairs) exceed its LDS space");
     }
     for (int b = 0; b < c->g.B; ++b) {
       a.t0[b] = t0[b];

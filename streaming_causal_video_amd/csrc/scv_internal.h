@@ -89,6 +89,19 @@ struct QkvArgs {
   double omega_t[kMaxAxisPairs];
 };
 
+// LDS bytes left to the fused projection's epilogue for its RoPE tables and
+// frame row bases: its two K-slice stages (x and weight rows, 64 deep) less
+// one 32-token staging block per wave (8 waves); tile = 128 * TB tokens.
+constexpr int qkv_table_capacity(int D, int TB) { return 2 * (TB * 128 * 64 * 2 + 2 * D * 64 * 2) - 8 * 32 * D * 2; }
+
+// LDS bytes those tables take for a tile of `tile` tokens: the time pairs of
+// every frame the tile can span, the height and width tables, one int32 row
+// base per frame.
+inline int64_t qkv_table_bytes(const Geometry& g, int tile) {
+  const int64_t nf = (tile - 1 + g.P - 1) / g.P + 1;
+  return (nf * (g.dt / 2) + int64_t(g.grid_h) * (g.dh / 2) + int64_t(g.grid_w) * (g.dw / 2)) * 8 + nf * 4;
+}
+
 // Attention kernel arguments (by value).
 struct AttnArgs {
   const void* q;

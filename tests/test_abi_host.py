@@ -344,6 +344,12 @@ def test_qkv_validation(lib):
     assert lib.scv_qkv_rope_append(h, p, 1536, p, p, t0(-5), 3, None) == -5
     assert lib.scv_qkv_rope_append(h, p, 1536, p, p, t0(5), 16, None) == -2  # more ring frames than R
     lib.scv_cache_destroy(h)
+    # a grid whose height and width tables (1000 x 21 + 1000 x 21 pairs) exceed
+    # the LDS the fused projection keeps them in
+    cfg, h = make_handle(lib, grid_h=1000, grid_w=1000, window_frames=2, chunk_frames=1)
+    assert lib.scv_qkv_rope_append(h, p, 32, p, p, t0(5), 1, None) == -2
+    assert "LDS" in B.last_error()
+    lib.scv_cache_destroy(h)
     cfg, h = make_handle(lib, dtype="fp32", head_dim=64, split=(24, 20, 20))
     assert lib.scv_qkv_rope_append(h, p, 64, p, p, t0(5), 3, None) == -3
     lib.scv_cache_destroy(h)
