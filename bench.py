@@ -387,7 +387,18 @@ def time_qkv(r, w, reps=20):
     us = back_to_back_us(fn, reps)
     flops = 2.0 * w.batch * w.query_rows * d_model * 3 * w.heads * w.head_dim
     tf = flops / (us * 1e-6) / 1e12
-    return {"us": us, "d_model": d_model, "flops": flops, "tflops": tf, "frac_mfma": tf / PEAK_TFLOPS["bf16"]}
+    # for scale, not part of the path: the library GEMM (torch.mm, hipBLASLt)
+    # of the same shape with contiguous operands and a plain bf16 output
+    # (no RoPE, no scatter into the ring)
+    import torch
+
+    x2 = x.reshape(-1, d_model)
+    wt = wq.t().contiguous()
+    out = torch.empty(x2.shape[0], wt.shape[1], device=x2.device, dtype=x2.dtype)
+    lib_us = back_to_back_us(lambda: torch.mm(x2, wt, out=out), reps)
+    del x2, wt, out
+    return {"us": us, "d_model": d_model, "flops": flops, "tflops": tf, "frac_mfma": tf / PEAK_TFLOPS["bf16"],
+            "library_gemm_us": lib_us, "library_gemm_frac_mfma": flops / (lib_us * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"]}
 
 
 def time_refresh_and_sink(r, w, reps=20):

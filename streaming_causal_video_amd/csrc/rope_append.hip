@@ -127,7 +127,9 @@ constexpr int kTokTile = 64;
 
 // One workgroup: tokens [p0, p0+64) of frame f of stream b, one head.
 // T: type of q, k, v inputs and cached values; QT: type of rotated q/k.
-template <typename T, typename QT, int D>
+// ALL: the chunk append (q rotated out, k rotated and v into the cache), so
+// every input and output exists and no load or store sits behind a branch.
+template <typename T, typename QT, int D, bool ALL>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   static_assert(sizeof(T) == sizeof(QT), "rotated and input elements share a size");
   constexpr int EPV = Vec16<T>::N;      // elements per 16-byte vector
@@ -145,11 +147,12 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   const int p0 = tile * kTokTile;
   const int nvalid = min(kTokTile, g.P - p0);
   const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
-  const bool to_cache = a.cache_k != nullptr;
-  const bool do_q = a.q_out != nullptr;
-  const bool do_k = a.k_in != nullptr;
-  const bool do_v = a.v_in != nullptr;
-  const bool need_angles = do_q || (do_k && a.rotate_k);
+  const bool to_cache = ALL || a.cache_k != nullptr;
+  const bool do_q = ALL || a.q_out != nullptr;
+  const bool do_k = ALL || a.k_in != nullptr;
+  const bool do_v = ALL || a.v_in != nullptr;
+  const bool rotate_k = ALL || a.rotate_k;
+  const bool need_angles = do_q || (do_k && rotate_k);
 
   __shared__ float2 tab_t[kMaxAxisPairs];
   __shared__ uint32_t vtile[kTokTile * ROW_U32];
@@ -167,72 +170,92 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 
   const int dg = threadIdx.x % TPR;
   const int64_t Ntok = int64_t(a.n_frames) * g.P;
-#pragma unroll 1
-  for (int pass = 0; pass < kTokTile / TPP; ++pass) {
+  // A pass covers TPP tokens.  Its inputs (q, k, v and the height and width
+  // cos/sin) are loaded one pass ahead: the loads of pass i+1 are issued
+  // before the rotations and stores of pass i, so a wave has two passes of
+  // loads in flight instead of waiting for q, then k, then v in turn.
+  constexpr int kPasses = kTokTile / TPP;
+  struct PassIn {
+    uint4 q, k, v;
+    float2 tv[EPV / 2], gv[EPV / 2];  // time (LDS) and height/width (global) entries
+  };
+  // Loads take no branch (a branch makes the compiler wait for every load
+  // in flight where it joins): tokens past the frame's end load a valid
+  // token of the tile instead (their results are dropped, their V rows
+  // zeroed), and each pair loads both its time entry (LDS) and its height or
+  // width entry (global) and keeps the one it needs.
+  auto load_pass = [&](int pass, PassIn& in) __attribute__((always_inline)) {
     const int tt = pass * TPP + int(threadIdx.x) / TPR;
-    const int p = p0 + tt;
     const bool valid = tt < nvalid;
+    const int p = valid ? p0 + tt : p0;
     const int64_t in_off = ((int64_t(b) * Ntok + int64_t(f) * g.P + p) * g.H + head) * D + dg * EPV;
-
-    float cs[EPV / 2], sn[EPV / 2];
-    if (need_angles && valid) {
+    in.q = in.k = in.v = make_uint4(0, 0, 0, 0);
+    if (do_q) in.q = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q_in) + in_off);
+    if (do_k) in.k = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + in_off);
+    if (do_v) in.v = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + in_off);
+    if (need_angles) {
       const int yy = p / g.grid_w, xx = p - (p / g.grid_w) * g.grid_w;
 #pragma unroll
       for (int i = 0; i < EPV / 2; ++i) {
         const int pj = dg * (EPV / 2) + i;
-        float2 t;
-        if (pj < pt)
-          t = tab_t[pj];
-        else if (pj < pth)
-          t = a.tab_h[yy * (g.dh / 2) + (pj - pt)];
-        else
-          t = a.tab_w[xx * (g.dw / 2) + (pj - pth)];
-        cs[i] = t.x;
-        sn[i] = t.y;
+        in.tv[i] = tab_t[pj < pt ? pj : 0];
+        const float2* gp = pj < pth ? a.tab_h + max(yy * (g.dh / 2) + (pj - pt), 0) : a.tab_w + (xx * (g.dw / 2) + (pj - pth));
+        in.gv[i] = *gp;
       }
     }
-    if (do_q && valid) {
-      float x[EPV], y[EPV];
-      unpack16<T>(*reinterpret_cast<const uint4*>(static_cast<const T*>(a.q_in) + in_off), x);
+  };
+  auto rotate = [&](const uint4 raw, const PassIn& in) __attribute__((always_inline)) {
+    float x[EPV], y[EPV];
+    unpack16<T>(raw, x);
 #pragma unroll
-      for (int i = 0; i < EPV / 2; ++i) {
-        y[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
-        y[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
-      }
-      *reinterpret_cast<uint4*>(static_cast<QT*>(a.q_out) + in_off) = pack16<QT>(y);
+    for (int i = 0; i < EPV / 2; ++i) {
+      const float2 cs = dg * (EPV / 2) + i < pt ? in.tv[i] : in.gv[i];
+      y[2 * i] = x[2 * i] * cs.x - x[2 * i + 1] * cs.y;
+      y[2 * i + 1] = x[2 * i] * cs.y + x[2 * i + 1] * cs.x;
     }
-    if (do_k && valid) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + in_off);
-      uint4 outv = raw;
-      if (a.rotate_k) {
-        float x[EPV], y[EPV];
-        unpack16<T>(raw, x);
+    return pack16<QT>(y);
+  };
+  // FULL: every token of the tile exists (all but the last tile of a frame
+  // whose token count is not a multiple of 64), so nothing in the loop
+  // depends on the lane: no branch for the compiler to wait at
+  auto passes = [&](auto full_c) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
+    PassIn in[2];
+    load_pass(0, in[0]);
 #pragma unroll
-        for (int i = 0; i < EPV / 2; ++i) {
-          y[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
-          y[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const PassIn& cur = in[pass & 1];
+      if (pass + 1 < kPasses) load_pass(pass + 1, in[(pass + 1) & 1]);
+      const int tt = pass * TPP + int(threadIdx.x) / TPR;
+      const int p = p0 + tt;
+      const bool valid = FULL || tt < nvalid;
+      const int64_t in_off = ((int64_t(b) * Ntok + int64_t(f) * g.P + p) * g.H + head) * D + dg * EPV;
+      if (do_q && valid) *reinterpret_cast<uint4*>(static_cast<QT*>(a.q_out) + in_off) = rotate(cur.q, cur);
+      if (do_k && valid) {
+        const uint4 outv = rotate_k ? rotate(cur.k, cur) : cur.k;
+        if (to_cache) {
+          const int64_t row = slot * g.slot_rows + p;
+          QT* dst = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + row) * D + dg * EPV;
+          *reinterpret_cast<uint4*>(dst) = outv;
+          if (also_sink) *reinterpret_cast<uint4*>(dst + (int64_t(sslot) - slot) * g.slot_rows * D) = outv;
+        } else {
+          *reinterpret_cast<uint4*>(static_cast<QT*>(a.k_out) + in_off) = outv;
         }
-        outv = pack16<QT>(y);
       }
-      if (to_cache) {
-        const int64_t row = slot * g.slot_rows + p;
-        QT* dst = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + row) * D + dg * EPV;
-        *reinterpret_cast<uint4*>(dst) = outv;
-        if (also_sink) *reinterpret_cast<uint4*>(dst + (int64_t(sslot) - slot) * g.slot_rows * D) = outv;
-      } else {
-        *reinterpret_cast<uint4*>(static_cast<QT*>(a.k_out) + in_off) = outv;
+      if (do_v) {
+        // rows past the frame's end are zero (they become slot padding)
+        uint32_t* r = &vtile[tt * ROW_U32 + dg * 4];
+        r[0] = valid ? cur.v.x : 0u;
+        r[1] = valid ? cur.v.y : 0u;
+        r[2] = valid ? cur.v.z : 0u;
+        r[3] = valid ? cur.v.w : 0u;
       }
     }
-    if (do_v) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (valid) raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + in_off);
-      uint32_t* r = &vtile[tt * ROW_U32 + dg * 4];
-      r[0] = raw.x;
-      r[1] = raw.y;
-      r[2] = raw.z;
-      r[3] = raw.w;
-    }
-  }
+  };
+  if (nvalid == kTokTile)
+    passes(std::true_type{});
+  else
+    passes(std::false_type{});
 
   if (do_v) {
     __syncthreads();
@@ -327,7 +350,11 @@ template <typename T, typename QT, int D>
 hipError_t launch_rope_append_t(const RopeArgs& a, hipStream_t s) {
   const int tiles_per_frame = (a.g.P + kTokTile - 1) / kTokTile;
   dim3 grid(tiles_per_frame * a.g.H, a.n_frames, a.g.B);
-  hipLaunchKernelGGL((rope_append_kernel<T, QT, D>), grid, dim3(256), 0, s, a);
+  const bool all = a.q_in && a.q_out && a.k_in && a.v_in && a.cache_k && a.rotate_k;
+  if (all)
+    hipLaunchKernelGGL((rope_append_kernel<T, QT, D, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((rope_append_kernel<T, QT, D, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
