@@ -314,22 +314,41 @@ __global__ __launch_bounds__(256) void rope_refresh_kernel(RefreshArgs a) {
   const int64_t r0 = int64_t(blockIdx.x) * kRefreshRows;
   const int nrows = int(min<int64_t>(kRefreshRows, g.rows_pad - r0));
   QT* base = static_cast<QT*>(a.cache_k) + ((int64_t(b) * g.H + head) * g.rows_pad + r0) * D;
-  for (int i = threadIdx.x; i < nrows * chunks; i += 256) {
-    const int r = i / chunks, c = i - (i / chunks) * chunks;
-    uint4* ptr = reinterpret_cast<uint4*>(base + int64_t(r) * D + c * EPV);
-    float x[EPV];
-    unpack16<QT>(*ptr, x);
+  // kU chunks per thread at a time: all their loads go out before the first
+  // rotation and store (a load cannot pass a store through the same
+  // pointer, so chunk by chunk each would wait a full memory latency)
+  constexpr int kU = 8;
+  const int n = nrows * chunks;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kU * 256) {
+    uint4 raw[kU];
+    uint4* ptr[kU];
+    int cc[kU];
 #pragma unroll
-    for (int e = 0; e < EPV / 2; ++e) {
-      const int j = c * (EPV / 2) + e;
-      if (j < pt) {
-        const float cs = tab[j].x, sn = tab[j].y;
-        const float u = x[2 * e], v = x[2 * e + 1];
-        x[2 * e] = u * cs + v * sn;
-        x[2 * e + 1] = v * cs - u * sn;
-      }
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(i0 + u * 256, n - 1);  // past the end: load a valid chunk, store nothing
+      const int r = i / chunks, c = i - (i / chunks) * chunks;
+      cc[u] = c;
+      ptr[u] = reinterpret_cast<uint4*>(base + int64_t(r) * D + c * EPV);
+      raw[u] = *ptr[u];
     }
-    *ptr = pack16<QT>(x);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (i0 + u * 256 >= n) break;
+      float x[EPV];
+      unpack16<QT>(raw[u], x);
+#pragma unroll
+      for (int e = 0; e < EPV / 2; ++e) {
+        // pairs past the time dims keep their values (a select, not a
+        // branch: lanes of one wave hold different chunks)
+        const int j = cc[u] * (EPV / 2) + e;
+        const bool on = j < pt;
+        const float2 t = tab[on ? j : 0];
+        const float uu = x[2 * e], v = x[2 * e + 1];
+        x[2 * e] = on ? uu * t.x + v * t.y : uu;
+        x[2 * e + 1] = on ? v * t.x - uu * t.y : v;
+      }
+      *ptr[u] = pack16<QT>(x);
+    }
   }
 }
 
