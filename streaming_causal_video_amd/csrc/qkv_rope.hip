@@ -104,7 +104,10 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const Geometry& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave / kTokGroups, wq = wave % kTokGroups;  // feature block, token group
+  // the two waves of a SIMD (w, w + 4) share a feature block and take token
+  // groups wq and wq + 2, so that in a workgroup with few tokens (the last
+  // token tile) the busy waves spread over the SIMDs
+  const int grp = wave % 2, wq = wave / 2;  // feature block, token group
   const int hl = lane >> 5, l32 = lane & 31;
   // Workgroups go to the 8 XCDs round robin; renumber them so that each
   // XCD runs a contiguous range of logical tiles, ordered in bands of
@@ -134,6 +137,9 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   const int sel = fb / g.H, head = fb - sel * g.H;  // 0: q, 1: k, 2: v
   const int Ntok = a.n_frames * g.P;
   const int m0 = mt * kQM;
+  // a wave whose feature block does not exist or whose tokens all lie past
+  // the end skips its MFMAs and epilogue, keeping its loads and barriers
+  const bool busy = fb_valid && m0 + 32 * TB * wq < Ntok;
   const int Dm = a.d_model;
   const int f_lo = m0 / g.P;
   const int pt = g.dt / 2, pth = (g.dt + g.dh) / 2;
@@ -249,6 +255,10 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
       // the first kSpread groups, so that a wave never stalls on issuing
       // them all at once behind the other waves' loads
       const bool load_next = kt >= 1 && kt + 1 < n_k;
+      if (!busy) {
+        if (load_next) issue(kt + 1, stg ^ 1);
+        return;
+      }
       int lrow = 0, c0 = 0;
       if (load_next) lane_parts(lrow, c0);
       bf16x8_t x[2][TB], w[2];
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
   for (int i = tid; i < nf; i += kThreads)
     row_base[i] = int(slot_of(f_lo + i) * g.slot_rows - int64_t(f_lo + i) * g.P);
   __syncthreads();
-  if (!fb_valid) return;
+  if (!busy) return;
   // t / P and p / grid_w through a float reciprocal and one correction step
   // (exact: tokens per call stay below 2^24, so the estimate is off by at
   // most one)
