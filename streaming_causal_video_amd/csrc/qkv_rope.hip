@@ -274,14 +274,18 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_kernel(QkvArgs a) {
 #pragma unroll
             for (int j = grp_i * DMA / kSpread; j < (grp_i + 1) * DMA / kSpread; ++j) issue_one(kt + 1, stg ^ 1, j, lrow, c0);
           }
-          // the reads first, then the group's MFMAs
-          if (db + 1 < DB) {
+          // the reads first, then the group's MFMAs; the next step's x
+          // fragments two groups ahead of their first use
+          if (db + 2 == DB && kk + 1 < NKK) {
+            read_x(kk + 1, x[(kk + 1) & 1]);
+            w[cur ^ 1] = read_w(kk, db + 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, TB + 1, 0);
+          } else if (db + 1 < DB) {
             w[cur ^ 1] = read_w(kk, db + 1);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           } else if (kk + 1 < NKK) {
-            read_x(kk + 1, x[(kk + 1) & 1]);
             w[cur ^ 1] = read_w(kk + 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, TB + 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           group(x[kk & 1], w[cur], db);
           __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
