@@ -16,10 +16,13 @@
 // operands are K-contiguous in memory (x rows, weight rows) and move global
 // -> LDS with the 16-byte direct loads of gfx950 into two stages of 64-deep
 // K slices (80 KB, or 64 KB, at D = 128): slice kt+1 loads while slice kt is
-// computed, one barrier per slice.  A slice row is 128 bytes, one whole
-// cache line of x or of the weight per load (32-deep slices, half lines,
-// measured 3-7% slower); a d_model that is an odd multiple of 32 ends with
-// a 32-deep slice.  The 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7),
+// computed (its loads spread over the first MFMA groups), one barrier per
+// slice; inside a slice each fragment is read one MFMA group ahead of its
+// use.  Workgroups are ordered in bands of token tiles so that the ones an
+// XCD runs at once share their x and weight slices in its L2.  A slice row
+// is 128 bytes, one whole cache line of x or of the weight per load
+// (32-deep slices, half lines, measured 3-7% slower); a d_model that is an
+// odd multiple of 32 ends with a 32-deep slice.  The 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7),
 // which puts any 16 consecutive rows of a fragment read on distinct banks.
 // For q and k the MFMA computes C^T (features as rows) so that each lane
 // holds the dim pairs (2j, 2j+1) of one token, which RoPE rotates in
@@ -27,8 +30,8 @@
 // consecutive tokens of one feature.
 // Epilogue: once every wave is done with the ring, it holds the RoPE
 // tables (time pairs of the tile's frames computed from fp64 angles, copies
-// of the height and width tables), so that every cos/sin comes from LDS, and
-// one staging area per wave: a wave rotates and rounds a 32-token block,
+// of the height and width tables), so that every cos/sin comes from LDS, the
+// ring row base of each of the tile's frames, and one staging area per wave: a wave rotates and rounds a 32-token block,
 // writes it into its area and reads it back as 16-byte pieces of whole rows
 // (a token's D features for q and k, 8 consecutive tokens of one feature for
 // the transposed value cache), so that the stores leave in contiguous
@@ -79,7 +82,8 @@ __device__ __forceinline__ uint16_t bits16(float x) {
 // One workgroup: 128*TB tokens of one stream x two feature blocks of D
 // features (two heads of q, k or v; the blocks may belong to different
 // ones); 8 waves, two per SIMD, so that one wave's MFMAs cover the other's
-// waits; each wave computes 32*TB tokens of one block.  TB = 3 (384 tokens,
+// waits; each wave computes 32*TB tokens of one block (the two waves of a
+// SIMD: the same block, token groups wq and wq + 2).  TB = 3 (384 tokens,
 // 160 KB of LDS) gives fewer, larger workgroups than TB = 2 (256 tokens);
 // the host picks the one whose grid fills the chip better.
 // (4 waves of 128x128 tiles -- half the LDS bytes per MFMA -- measured 1.5x

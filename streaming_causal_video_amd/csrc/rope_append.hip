@@ -19,7 +19,9 @@
 //    through LDS and leaves as 16-byte row-contiguous stores;
 //  * the time-axis cos/sin of the workgroup's frame is evaluated in fp64 at
 //    workgroup start (one entry per lane), the row/column tables are static
-//    per cache and read through L1/L2.
+//    per cache and read through L1/L2;
+//  * a workgroup's four 16-token passes load their inputs one pass ahead,
+//    with no load behind a branch, so two passes of loads are in flight.
 #include <type_traits>
 
 #include "scv_internal.h"
