@@ -685,7 +685,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   auto finish_softmax = [&](floatx16& s, bf16x8 (&p)[2], float& rs, auto next_c,
                             floatx16& s_next) __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_c)::value;
-    if (__any((rs > kPBound) || (m_run == -INFINITY))) {
+    // (marked unlikely so that the rescale is laid out away from the key
+    // loop and the common path runs on without a taken branch)
+    if (__builtin_expect(__any((rs > kPBound) || (m_run == -INFINITY)), 0)) {
       // row max with v_max3_f32 issued directly (see vmax3); the fence makes
       // the wait states an MFMA result needs before such reads explicit
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s));
@@ -764,10 +766,15 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = j * EPC; e < (j + 1) * EPC; ++e) {
         const float f = fast_exp2(s_prv[e]);
-        acc[e & 1] += f;
-        // the empty volatile asm keeps the sum (and below the bf16 pair) in
-        // this group instead of letting them sink to the end of the step
-        asm volatile("" : "+v"(acc[e & 1]));
+        // each chain starts from its first exponential (no add to zero); the
+        // empty volatile asm keeps the sum (and below the bf16 pair) in this
+        // group instead of letting them sink to the end of the step
+        if (e < 2) {
+          acc[e & 1] = f;
+        } else {
+          acc[e & 1] += f;
+          asm volatile("" : "+v"(acc[e & 1]));
+        }
         if (e & 1) {
           const bf16x2 pr = {static_cast<__bf16>(fprev), static_cast<__bf16>(f)};
           uint32_t w = __builtin_bit_cast(uint32_t, pr);
@@ -872,9 +879,17 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     auto real = [&](int t) __attribute__((always_inline)) { return t < t_end ? t : t_begin; };
     auto barrier_v = [&](int st) __attribute__((always_inline)) {
       wait_vm<KV + T::K_DMA>();
-      __syncthreads();
+      // A bare s_barrier: __syncthreads() would first wait for this wave's
+      // LDS reads in flight, the next step's first fragments, which come from
+      // V^T of visit v-1; the loads after this barrier only overwrite the
+      // stages of V^T of visit v-2 and K of visit v-1, whose reads all
+      // completed before their MFMAs.  The empty asm statements keep the
+      // compiler from moving memory accesses across the barrier.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       tv3 = next_or_end(tv2, &f3);
-      if (!active) {
+      if (__builtin_expect(!active, 0)) {
         issue_v(real(tv2), (st + 2) % 4);
         issue_k(real(tv3), (st + 3) % 4);
       }
@@ -942,7 +957,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) asm volatile("" : "+v"(voff[g4]));
       barrier_v(st);
-      if (active) {
+      if (__builtin_expect(active, 1)) {
         float rs;
         // step 2v-1: P V of unit 2v-2, S^T of unit 2v, softmax of unit 2v-1
         mask_if(sb[1], tp, fp, 1);
