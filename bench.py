@@ -255,15 +255,22 @@ def read_clock_samples(h, t_lo, t_hi):
 
 def load_window(r, seconds=3.0):
     """Back-to-back attention launches for `seconds` (wall clock); returns
-    the window."""
+    the window and the mean time per launch over it (HIP events on the
+    launch stream around all of its launches)."""
     import torch
 
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
     t_lo = time.time()
+    e0.record()
     while time.time() < t_lo + seconds:
         for _ in range(100):
             r.attend()
+        n += 100
         torch.cuda.synchronize()
-    return t_lo + 0.5, time.time()
+    e1.record()
+    torch.cuda.synchronize()
+    return (t_lo + 0.5, time.time()), {"ms": e0.elapsed_time(e1) / n, "launches": n}
 
 
 def cold_step_ms(r, reps=5, flush_bytes=512 << 20):
@@ -569,7 +576,14 @@ def main():
     # the projection first: the refreshes move time positions below t0
     out["next_rows"] = {"qkv_rope_append": time_qkv(r, w)} if w.dtype == "bf16" else {}
     out["next_rows"].update(time_refresh_and_sink(r, w))
-    out["sclk_under_load"] = read_clock_samples(clock_sampler, *load_window(r)) if clock_sampler else None
+    out["sclk_under_load"] = None
+    if clock_sampler:
+        # after the timed steps: the same attention launch back to back for
+        # 3 s, past the shader clock's start-up transient (reported beside
+        # `attn_ms`, not used for `value`)
+        window, sustained = load_window(r)
+        out["sclk_under_load"] = read_clock_samples(clock_sampler, *window)
+        out["attn_ms_sustained"] = dict(sustained, note="attention alone, launched back to back for 3 s after the timed steps (HIP events around all launches; includes the gaps between them)")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
