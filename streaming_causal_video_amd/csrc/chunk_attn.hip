@@ -161,7 +161,7 @@ __device__ __forceinline__ bool tile_full(const Geometry& g, uint64_t slots, int
 // within each wave instead of in alternating phases.
 // Tiles of 64 keys move global -> LDS through the 16-byte direct loads of
 // gfx950 (no VGPR staging) into K and V^T rings of 4 stages, two tiles
-// ahead of use, with one barrier per tile.  In LDS, K rows are permuted inside each 16-row
+// ahead of use, with one barrier per two tiles.  In LDS, K rows are permuted inside each 16-row
 // group (bits 2 and 3 of the row index swapped) so that the S^T accumulator
 // of lane half h holds, per 16-key group, exactly keys 8h..8h+7 of that
 // group: P^T then pairs with V^T read in natural key order (one 16-byte read
@@ -797,11 +797,12 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
   // wave in 32-key units: step u runs the MFMAs of P V of unit u-1 and of
   // S^T of unit u+1 with the softmax of unit u interleaved between them
   // (the SIMD's two waves run such steps side by side).  Visit v's tiles: K
-  // in K stage v % 4, V^T in V stage v % 4.  Barrier B_v (before the steps
-  // 2v-1 and 2v, which compute S^T of visit v) waits for K and V^T of visit
-  // v, loaded two barriers earlier, then starts the loads of V^T of visit
-  // v+2 and K of visit v+3 into the stages of visits v-2 and v-1, which
-  // every wave finished before B_v.  Tiles that are only partly visible
+  // in K stage v % 4, V^T in V stage v % 4.  Before even visits v a barrier
+  // B_v (before the steps 2v-1 and 2v, which compute S^T of visit v) waits
+  // for the loads started at B_{v-2} -- K of visits v and v+1, V^T of
+  // visits v-1 and v -- then starts those of the next two visits' K and V^T
+  // (V^T of v+1 and v+2, K of v+2 and v+3) into stages whose tiles every
+  // wave finished before B_v; odd visits pass no barrier.  Tiles that are only partly visible
   // (slot padding, window edges, the row tail) have their hidden keys
   // masked before their softmax.
   RunWalk walk;
@@ -870,41 +871,54 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     int tv1 = next_or_end(tv0, &f1);
     int tv2 = next_or_end(tv1, &f2);
     int tv3 = t_end;
-    // B_v: wait for K and V^T of visit v (loads after V^T of v: K of v+1,
-    // V^T of v+1 and K of v+2), barrier, then the loads of V^T of v+2 and K
-    // of v+3.  st = v % 4.
+    // B_v (even visits v only): wait for every load in flight -- K of
+    // visits v and v+1, V^T of visits v-1 and v, issued at B_{v-2} --
+    // barrier, then the loads of V^T of visits v+1 and v+2 and K of visits
+    // v+2 and v+3 into the stages of V^T of v-3 and v-2 and K of v-2 and
+    // v-1, which every wave finished before B_v.  st = v % 4.
     // Every barrier issues the same number of loads: a visit that does not
     // exist loads the first tile again into its (free) stage, so the wait
     // counts need no case analysis and the loads need no branch.
     auto real = [&](int t) __attribute__((always_inline)) { return t < t_end ? t : t_begin; };
     auto barrier_v = [&](int st) __attribute__((always_inline)) {
-      wait_vm<KV + T::K_DMA>();
+      wait_vm<0>();
       // A bare s_barrier: __syncthreads() would first wait for this wave's
       // LDS reads in flight, the next step's first fragments, which come from
-      // V^T of visit v-1; the loads after this barrier only overwrite the
-      // stages of V^T of visit v-2 and K of visit v-1, whose reads all
-      // completed before their MFMAs.  The empty asm statements keep the
-      // compiler from moving memory accesses across the barrier.
+      // V^T of visit v-1; the loads after this barrier do not overwrite that
+      // stage, and every read of the stages they do overwrite completed
+      // before its MFMA.  The empty asm statements keep the compiler from
+      // moving memory accesses across the barrier.
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       tv3 = next_or_end(tv2, &f3);
       if (__builtin_expect(!active, 0)) {
+        issue_v(real(tv1), (st + 1) % 4);
         issue_v(real(tv2), (st + 2) % 4);
+        issue_k(real(tv2), (st + 2) % 4);
         issue_k(real(tv3), (st + 3) % 4);
       }
     };
     // The same loads issued by a wave with steps: one per odd MFMA group of
-    // the step after the barrier, so that their issue overlaps the MFMAs.
-    auto loads_in_step = [&](int st) __attribute__((always_inline)) {
-      const int tv = real(tv2), tk = real(tv3), sv = (st + 2) & 3, sk = (st + 3) & 3;
+    // the step after the barrier (after B_0, of the two steps that follow,
+    // which hold the S^T MFMAs only), so that their issue overlaps the MFMAs;
+    // load number base + j / 2 goes with group j.
+    static_assert(2 * (T::K_DMA + T::V_DMA) <= (2 * DB + KS) / 2, "one load per odd MFMA group of a step");
+    static_assert(2 * (T::K_DMA + T::V_DMA) <= 2 * (KS / 2), "one load per odd MFMA group of the first two steps");
+    auto loads_in_step = [&](int st, int base) __attribute__((always_inline)) {
+      const int t1 = real(tv1), t2 = real(tv2), t3 = real(tv3);
+      const int s1 = (st + 1) & 3, s2 = (st + 2) & 3, s3 = (st + 3) & 3;
       return [=, &issue_v1, &issue_k1](int j) __attribute__((always_inline)) {
         if (j & 1) {
-          const int i = j >> 1;
+          const int i = base + (j >> 1);
           if (i < T::V_DMA)
-            issue_v1(tv, sv, i);
-          else if (i < T::V_DMA + T::K_DMA)
-            issue_k1(tk, sk, i - T::V_DMA);
+            issue_v1(t1, s1, i);
+          else if (i < 2 * T::V_DMA)
+            issue_v1(t2, s2, i - T::V_DMA);
+          else if (i < 2 * T::V_DMA + T::K_DMA)
+            issue_k1(t2, s2, i - 2 * T::V_DMA);
+          else if (i < 2 * T::V_DMA + 2 * T::K_DMA)
+            issue_k1(t3, s3, i - 2 * T::V_DMA - T::K_DMA);
         }
       };
     };
@@ -925,20 +939,18 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     issue_k(tv0, 0);
     issue_v(tv0, 0);
     issue_k(real(tv1), 1);
-    issue_v(real(tv1), 1);
-    issue_k(real(tv2), 2);
     barrier_v(0);
     if (active) {
       // S^T of unit 0 alone (the fragment ring then holds the first
       // fragments of the next step)
       float rs;
       step_ops(C0{}, CQK{}, No{}, Yes{}, Yes{}, Src{false, 0, 0}, Src{false, 0, 0}, Src{false, 0, 1}, pb[1], sb[0],
-               sb[1], pb[1], rs, loads_in_step(0));
+               sb[1], pb[1], rs, loads_in_step(0, 0));
       mask_if(sb[0], tv0, f0, 0);
       // S^T of unit 1 with the softmax of unit 0; then the first fragments
       // of P V of unit 0
       step_ops(C0{}, CQK{}, Yes{}, No{}, Yes{}, Src{false, 0, 0}, Src{false, 0, 1}, Src{true, 0, 0}, pb[1], sb[1],
-               sb[0], pb[0], rs, no_extra);
+               sb[0], pb[0], rs, loads_in_step(0, KS / 2));
       // the softmax of unit 0 ran against the reference that existed before
       // it (none): finish it now
       finish_softmax(sb[0], pb[0], rs, Yes{}, sb[1]);
@@ -956,13 +968,23 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(koff[kk]));
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) asm volatile("" : "+v"(voff[g4]));
-      barrier_v(st);
+      constexpr bool kSync = (st & 1) == 0;  // a barrier before even visits only
+      if constexpr (kSync)
+        barrier_v(st);
+      else
+        tv3 = next_or_end(tv2, &f3);
+      auto first_extra = [&]() __attribute__((always_inline)) {
+        if constexpr (kSync)
+          return loads_in_step(st, 0);
+        else
+          return no_extra;
+      };
       if (__builtin_expect(active, 1)) {
         float rs;
         // step 2v-1: P V of unit 2v-2, S^T of unit 2v, softmax of unit 2v-1
         mask_if(sb[1], tp, fp, 1);
         step_ops(CPV{}, CQK{}, Yes{}, No{}, Yes{}, Src{true, sp, 0}, Src{false, st, 0}, Src{true, sp, 1}, pb[0],
-                 sb[0], sb[1], pb[1], rs, loads_in_step(st));
+                 sb[0], sb[1], pb[1], rs, first_extra());
         finish_softmax(sb[1], pb[1], rs, Yes{}, sb[0]);
         // step 2v: P V of unit 2v-1, S^T of unit 2v+1, softmax of unit 2v
         mask_if(sb[0], tv0, f0, 0);
@@ -984,7 +1006,15 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       visit(std::integral_constant<int, 0>{});
     }
     // after the last visit v = n-1 (stage (st + 3) % 4): the softmax of unit
-    // 2n-1 with P V of unit 2n-2, then P V of unit 2n-1
+    // 2n-1 with P V of unit 2n-2, then P V of unit 2n-1.  When n-1 is odd,
+    // V^T of visit n-1 was loaded at the last barrier, B_{n-2}: wait for it
+    // (every wave's share) first.
+    if ((st & 1) == 0) {
+      wait_vm<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
     if (active) {
       const int sl = (st + 3) & 3;
       float rs;
