@@ -339,7 +339,7 @@ struct RunWalk {
   __device__ __forceinline__ int next(const Geometry& g, uint64_t slots, bool first, bool* full) {
     if (first) {
       if (!valid) return t_end;
-    } else if (t < last) {
+    } else if (__builtin_expect(t < last, 1)) {  // inside a run: the common case
       ++t;
     } else if (!open(g, slots, s_next, t + 1)) {
       t = t_end;
@@ -859,7 +859,9 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     };
     auto mask_if = [&](floatx16& s, int t, bool full, int h) __attribute__((always_inline)) {
       if constexpr (kMasked) {
-        if (!full) mask(s, t, h);
+        // partial tiles are few (run edges): their masking stays off the
+        // loop's straight-line path
+        if (__builtin_expect(!full, 0)) mask(s, t, h);
       }
     };
     constexpr int KV = T::K_DMA + T::V_DMA;
