@@ -981,16 +981,23 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
         else
           return no_extra;
       };
+      // No fragment read crosses a barrier: the tiles a step after B_v
+      // reads first (V^T of visit v-1) are only known to have landed in
+      // every wave's share once B_v has passed.  So the first step of an
+      // even visit reads its own first fragments, and the last step of an
+      // odd visit (the one before the next barrier) reads none ahead.
+      using OwnA = std::integral_constant<bool, kSync>;
+      using NxB = std::integral_constant<bool, kSync>;
       if (__builtin_expect(active, 1)) {
         float rs;
         // step 2v-1: P V of unit 2v-2, S^T of unit 2v, softmax of unit 2v-1
         mask_if(sb[1], tp, fp, 1);
-        step_ops(CPV{}, CQK{}, Yes{}, No{}, Yes{}, Src{true, sp, 0}, Src{false, st, 0}, Src{true, sp, 1}, pb[0],
+        step_ops(CPV{}, CQK{}, Yes{}, OwnA{}, Yes{}, Src{true, sp, 0}, Src{false, st, 0}, Src{true, sp, 1}, pb[0],
                  sb[0], sb[1], pb[1], rs, first_extra());
         finish_softmax(sb[1], pb[1], rs, Yes{}, sb[0]);
         // step 2v: P V of unit 2v-1, S^T of unit 2v+1, softmax of unit 2v
         mask_if(sb[0], tv0, f0, 0);
-        step_ops(CPV{}, CQK{}, Yes{}, No{}, Yes{}, Src{true, sp, 1}, Src{false, st, 1}, Src{true, st, 0}, pb[1],
+        step_ops(CPV{}, CQK{}, Yes{}, No{}, NxB{}, Src{true, sp, 1}, Src{false, st, 1}, Src{true, st, 0}, pb[1],
                  sb[1], sb[0], pb[0], rs, no_extra);
         finish_softmax(sb[0], pb[0], rs, Yes{}, sb[1]);
       }
@@ -1010,8 +1017,10 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
     // after the last visit v = n-1 (stage (st + 3) % 4): the softmax of unit
     // 2n-1 with P V of unit 2n-2, then P V of unit 2n-1.  When n-1 is odd,
     // V^T of visit n-1 was loaded at the last barrier, B_{n-2}: wait for it
-    // (every wave's share) first.
-    if ((st & 1) == 0) {
+    // (every wave's share) first; its last step read no fragments ahead, so
+    // the first step here reads its own.
+    const bool last_odd = (st & 1) == 0;
+    if (last_odd) {
       wait_vm<0>();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -1021,8 +1030,12 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_bf16_kernel(AttnArgs a) {
       const int sl = (st + 3) & 3;
       float rs;
       mask_if(sb[1], tp, fp, 1);
-      step_ops(CPV{}, C0{}, Yes{}, No{}, Yes{}, Src{true, sl, 0}, Src{false, 0, 0}, Src{true, sl, 1}, pb[0], sb[0],
-               sb[1], pb[1], rs, no_extra);
+      if (last_odd)
+        step_ops(CPV{}, C0{}, Yes{}, Yes{}, Yes{}, Src{true, sl, 0}, Src{false, 0, 0}, Src{true, sl, 1}, pb[0], sb[0],
+                 sb[1], pb[1], rs, no_extra);
+      else
+        step_ops(CPV{}, C0{}, Yes{}, No{}, Yes{}, Src{true, sl, 0}, Src{false, 0, 0}, Src{true, sl, 1}, pb[0], sb[0],
+                 sb[1], pb[1], rs, no_extra);
       finish_softmax(sb[1], pb[1], rs, No{}, sb[0]);
       step_ops(CPV{}, C0{}, No{}, No{}, No{}, Src{true, sl, 1}, Src{false, 0, 0}, Src{false, 0, 0}, pb[1], sb[0],
                sb[1], pb[0], rs, no_extra);
