@@ -36,11 +36,11 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md (grid schedule, one launch)
-    "wan1.3b-480p": {"source": "f8a6e032d792e320", "kv_splits": 1, "bytes_per_launch": 378286080},
+    "wan1.3b-480p": {"source": "e7aa9d0fae5d7330", "kv_splits": 1, "bytes_per_launch": 380914995},
     # profiles/chunk_attn_wan13b_720p_balanced.md (balanced schedule with
     # whole-item rounds: the attention launch and its merge launch, as timed
     # together)
-    "wan1.3b-720p": {"source": "f8a6e032d792e320", "kv_splits": -2, "bytes_per_launch": 1002530304},
+    "wan1.3b-720p": {"source": "e7aa9d0fae5d7330", "kv_splits": -2, "bytes_per_launch": 1004955853},
 }
 KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
 
