@@ -36,13 +36,17 @@ HBM_PEAK_GBS = 8000.0
 # they were taken on: any other source hash reports null.
 MEASURED_TRAFFIC = {
     # profiles/chunk_attn_wan13b_480p.md (grid schedule, one launch)
-    "wan1.3b-480p": {"source": "e7aa9d0fae5d7330", "kv_splits": 1, "bytes_per_launch": 380914995},
+    "wan1.3b-480p": {"source": "39c1999d5fe07a07", "kv_splits": 1, "bytes_per_launch": 380914995},
     # profiles/chunk_attn_wan13b_720p_balanced.md (balanced schedule with
     # whole-item rounds: the attention launch and its merge launch, as timed
     # together)
-    "wan1.3b-720p": {"source": "e7aa9d0fae5d7330", "kv_splits": -2, "bytes_per_launch": 1004955853},
+    "wan1.3b-720p": {"source": "39c1999d5fe07a07", "kv_splits": -2, "bytes_per_launch": 972712435},
 }
-KERNEL_SOURCES = ["streaming_causal_video_amd/csrc/chunk_attn.hip", "streaming_causal_video_amd/csrc/scv_internal.h"]
+KERNEL_SOURCES = [
+    "streaming_causal_video_amd/csrc/chunk_attn.hip",
+    "streaming_causal_video_amd/csrc/scv_internal.h",
+    "streaming_causal_video_amd/csrc/scv_abi.cpp",  # the schedule the host picks
+]
 
 
 def kernel_source_hash():

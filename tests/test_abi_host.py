@@ -262,14 +262,17 @@ def test_auto_splits_respect_workspace_and_t0(lib):
     assert lib.scv_attention_splits(h, t0(-1), 3, 0, big) == 0
     assert lib.scv_attention_splits(h, t0(20000), 3, -3, big) == 0
     # whole-item rounds on request: 516 items = 2 rounds of 256 whole items
-    # + 4 items cut into 256 ranges, 768 workgroups as for the equal cut
+    # + 4 items cut into 128 ranges (half the compute units), 640 workgroups
+    # against 768 for the equal cut
     assert lib.scv_attention_splits(h, t0(20000), 3, -2, big) == -2
-    assert lib.scv_attention_request_workspace_bytes(h, t0(20000), 3, -2) == lean_ws(768)
-    assert lib.scv_attention_workspace_bytes(h, 3, -2) == lean_ws(768)
+    assert lib.scv_attention_request_workspace_bytes(h, t0(20000), 3, -2) == lean_ws(640)
+    assert lib.scv_attention_workspace_bytes(h, 3, -2) == lean_ws(640)
     lean = lib.scv_attention_workspace_bytes(h, 3, -1)
-    assert lean > 0
-    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean) == -2  # same 768 workgroups
-    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean - 1) > 1  # key splits that fit
+    assert lean == lean_ws(768)
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, lean) == -2
+    rounds_ws = lean_ws(640)
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, rounds_ws) == -2  # fits exactly
+    assert lib.scv_attention_splits(h, t0(20000), 3, 0, rounds_ws - 1) > 1  # key splits that fit
     lib.scv_cache_destroy(h)
 
 
@@ -301,9 +304,10 @@ def test_balanced_schedule_plan(lib):
     assert lib.scv_attention_splits(h, t0(1000), 3, 0, big) == 1
     assert lib.scv_attention_request_workspace_bytes(h, t0(1000), 3, -1) == lean_ws(768)
     lib.scv_cache_destroy(h)
-    # 720p: 516 items of 675 tiles -> 3 ranges per compute unit (453.5 units)
+    # 720p: the automatic choice is whole-item rounds, 2 x 256 whole items
+    # and the 4 left-over items cut into 128 ranges
     cfg, h = make_handle(lib, grid_h=45, grid_w=80, window_frames=8)
-    assert lib.scv_attention_request_workspace_bytes(h, t0(20000), 3, 0) == lean_ws(768)
+    assert lib.scv_attention_request_workspace_bytes(h, t0(20000), 3, 0) == lean_ws(640)
     lib.scv_cache_destroy(h)
     # fp32 has no balanced kernel: -1 falls back to one split
     cfg, h = make_handle(lib, dtype="fp32", head_dim=64, split=(24, 20, 20))
